@@ -1,0 +1,231 @@
+"""Plain float64 definition of the causal lightning indexer, dense and group-shared.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow on purpose: one
+query or one group at a time, one library matmul per step, no blocking or
+fusion, so that each function can be checked by eye against what it cites.
+
+Sources (web pages; cited by title and section):
+
+* "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention"
+  (aiqbench.com), Abstract: the indexer scores every preceding token of each
+  query and keeps a per-query top-k; PIVOT forms fixed-size groups of
+  consecutive queries, aggregates each group into one proxy query, does one
+  shared full-prefix scan to a candidate set, and then either re-scores the
+  candidates with each member's own indexer and selects each member's own
+  top-k (Refine) or shares the proxy's top-k with the whole group (Reuse).
+* "IndexCache: Accelerating Sparse Attention via Cross-Layer Index Reuse"
+  (wispaper.ai), "The Quadratic Tax of Sparse Attention": the lightning
+  indexer scores all preceding tokens to pick the top-k.
+* "ADIndex Restructures Sparse-Attention Indexing with Group-Level
+  Distillation" (zicq.com), "Why the Indexer Becomes the Bottleneck": the
+  scan covers the whole causal prefix of every query, in prefill and decode.
+* "MLI Restructures DeepSeek Sparse Attention ..." (zicq.com), "Core Idea":
+  k = 2048 positions are kept per query.
+* "AttentionIndex Architecture ..." (globaltechdigest.blogspot.com), "KEY
+  FINDINGS": recall is measured against the exhaustive top-k.
+
+Readings where the pages are silent (each is also listed in the design notes):
+
+* Score.  No page prints the indexer's formula.  The reading is the DeepSeek
+  lightning-indexer form I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]),
+  with no extra constant (a positive constant would change no top-k).
+* Causality.  "Preceding" is read inclusively: key s is visible to query t
+  iff s <= pos(t) = q_pos0 + t (q_pos0 = 0 in prefill, n_k - n_q in decode,
+  where the cache already holds the new tokens' keys).
+* Ties.  Order by (score descending, key index ascending); equal means exact
+  equality, so -0.0 == +0.0.  Output rows are sets (padded with -1).
+* Fewer candidates than k.  Keep all of them.
+* Proxy.  "Aggregates" is read as the arithmetic mean of the members' real
+  (dequantised) q and of their head weights w; the proxy scan covers the
+  prefix of the group's last member.  The proxy is stored for the scan in
+  bfloat16 (round to nearest even) for bf16 and fp8 inputs and in float32
+  for float32 inputs; see ``round_proxy``.
+* Causality inside a group.  Refine and Reuse drop candidates beyond the
+  member's own position; Reuse does not refill the dropped slots.
+"""
+
+import numpy as np
+
+from .formats import f64_to_bf16_bits_rne, bf16_bits_to_f64
+
+
+# ----------------------------------------------------------------------------
+# scoring
+
+
+def causal_scores(q, k, w, limits):
+    """Score rows with a per-row causal limit.
+
+    q : [R, H, d] float64 real query values (R rows), k : [n_k, d] float64,
+    w : [R, H] float64, limits : [R] int, row r sees keys 0..limits[r].
+    Returns [R, n_k] float64; entries beyond a row's limit are -inf (excluded).
+    """
+    R = q.shape[0]
+    n_k = k.shape[0]
+    out = np.full((R, n_k), -np.inf)
+    for r in range(R):
+        p = int(limits[r])
+        if p < 0:
+            continue
+        x = k[: p + 1] @ q[r].T  # [p+1, H]: q[r,h,:] . k[s,:]
+        out[r, : p + 1] = np.maximum(x, 0.0) @ w[r]  # sum_h w[r,h] * relu(x[s,h])
+    return out
+
+
+def dense_scores(q, k, w, q_pos0):
+    """I[t, s] for one sequence: query t sees keys s <= pos(t) = q_pos0 + t."""
+    n_q = q.shape[0]
+    return causal_scores(q, k, w, q_pos0 + np.arange(n_q))
+
+
+# ----------------------------------------------------------------------------
+# selection
+
+
+def select_topk(values, index, k):
+    """The first min(k, n) of ``index`` ordered by (value descending, index ascending)."""
+    values = np.asarray(values, dtype=np.float64)
+    index = np.asarray(index, dtype=np.int64)
+    order = np.lexsort((index, -values))
+    return index[order[: min(k, index.size)]]
+
+
+def _pad(rows, width):
+    out = np.full((len(rows), width), -1, dtype=np.int64)
+    for i, r in enumerate(rows):
+        out[i, : len(r)] = r
+    return out
+
+
+def dense_topk(q, k, w, q_pos0, topk, scores=None):
+    """Per-query top-k over the causal prefix, one sequence; [n_q, topk] padded with -1.
+
+    ``scores`` may supply precomputed rows (e.g. a GPU dump, to check a select
+    bit-exactly on the same values); masked entries are never selected.
+    """
+    I = dense_scores(q, k, w, q_pos0) if scores is None else np.asarray(scores, np.float64)
+    rows = []
+    for t in range(I.shape[0]):
+        p = q_pos0 + t
+        rows.append(select_topk(I[t, : p + 1], np.arange(p + 1), topk))
+    return _pad(rows, topk)
+
+
+# ----------------------------------------------------------------------------
+# group-shared (PIVOT) indexing
+
+
+def group_bounds(n_q, group):
+    """Fixed-size groups of consecutive queries: [(first, last_exclusive), ...]."""
+    return [(g0, min(g0 + group, n_q)) for g0 in range(0, n_q, group)]
+
+
+def proxy_limits(n_q, group, q_pos0):
+    """Each group's scan covers the prefix of its last member: pos(t_last)."""
+    return np.array([q_pos0 + e - 1 for (_, e) in group_bounds(n_q, group)], dtype=np.int64)
+
+
+def proxy_means(q, w, group):
+    """Proxy query and weights: the mean over the group's members (float64)."""
+    gb = group_bounds(q.shape[0], group)
+    qbar = np.stack([q[a:b].mean(axis=0) for (a, b) in gb])
+    wbar = np.stack([w[a:b].mean(axis=0) for (a, b) in gb])
+    return qbar, wbar
+
+
+def round_proxy(qbar, wbar, q_fmt):
+    """The proxy's storage format for the scan (a reading, see module docstring).
+
+    q: float32 for float32 inputs, bfloat16 (nearest, ties to even) otherwise;
+    w: float32.  Returns float64 values of the stored proxy.
+    """
+    if q_fmt == "f32":
+        qs = qbar.astype(np.float32).astype(np.float64)
+    else:
+        qs = bf16_bits_to_f64(f64_to_bf16_bits_rne(qbar))
+    return qs, wbar.astype(np.float32).astype(np.float64)
+
+
+def proxy_scores(qbar, wbar, k, limits):
+    """P[g, s] = sum_h wbar[g,h] relu(qbar[g,h,:] . k[s,:]) for s <= limits[g]."""
+    return causal_scores(qbar, k, wbar, limits)
+
+
+def proxy_candidates(P, limits, n_cand):
+    """cand[g] = top min(C, limit+1) of the group's prefix by (-P, s); padded with -1."""
+    rows = []
+    for g in range(P.shape[0]):
+        p = int(limits[g])
+        rows.append(select_topk(P[g, : p + 1], np.arange(p + 1), n_cand))
+    return _pad(rows, n_cand)
+
+
+def refine_topk(q, k, w, cand, group, q_pos0, topk, scores=None):
+    """PIVOT-Refine: each member re-scores its group's candidates with its own
+    indexer and keeps its own top min(k, |V_t|), V_t = cand(g) within [0, pos(t)].
+
+    cand : [n_g, C] int, -1 (or any negative) = empty slot.  ``scores`` may
+    supply [n_q, C] per-candidate values to select from instead of computing
+    them (to check a select on a GPU's own values).
+    """
+    n_q = q.shape[0]
+    rows = []
+    for g, (a, b) in enumerate(group_bounds(n_q, group)):
+        c = np.asarray(cand[g], dtype=np.int64)
+        for t in range(a, b):
+            p = q_pos0 + t
+            keep = (c >= 0) & (c <= p)
+            v = c[keep]
+            if scores is None:
+                vals = np.maximum(k[v] @ q[t].T, 0.0) @ w[t] if v.size else np.zeros(0)
+            else:
+                vals = np.asarray(scores[t], np.float64)[keep]
+            rows.append(select_topk(vals, v, topk))
+    return _pad(rows, topk)
+
+
+def reuse_topk(proxy_top, group, q_pos0, n_q, topk):
+    """PIVOT-Reuse: member t keeps the proxy's top-k entries that are <= pos(t), no refill."""
+    rows = []
+    for g, (a, b) in enumerate(group_bounds(n_q, group)):
+        r = np.asarray(proxy_top[g], dtype=np.int64)
+        r = r[r >= 0][:topk]
+        for t in range(a, b):
+            rows.append(r[r <= q_pos0 + t])
+    return _pad(rows, topk)
+
+
+def grouped_reference(q, k, w, q_pos0, group, n_cand, topk, variant, q_fmt):
+    """Whole group-shared pipeline for one sequence, entirely in the oracle.
+
+    variant "refine": proxy -> scan -> top-C candidates -> per-member re-score
+    and top-k.  variant "reuse": proxy -> scan -> top-k shared by the group.
+    Returns (out [n_q, topk], cand [n_g, C or topk], proxy q, proxy w).
+    """
+    n_q = q.shape[0]
+    qbar, wbar = round_proxy(*proxy_means(q, w, group), q_fmt)
+    lim = proxy_limits(n_q, group, q_pos0)
+    P = proxy_scores(qbar, wbar, k, lim)
+    if variant == "refine":
+        cand = proxy_candidates(P, lim, n_cand)
+        out = refine_topk(q, k, w, cand, group, q_pos0, topk)
+    elif variant == "reuse":
+        cand = proxy_candidates(P, lim, topk)
+        out = reuse_topk(cand, group, q_pos0, n_q, topk)
+    else:
+        raise ValueError(variant)
+    return out, cand, qbar, wbar
+
+
+# ----------------------------------------------------------------------------
+# measurement
+
+
+def recall(approx, exact):
+    """recall_t = |approx_t & exact_t| / |exact_t| per query (-1 entries ignored)."""
+    out = np.empty(exact.shape[0])
+    for t in range(exact.shape[0]):
+        e = set(int(x) for x in exact[t] if x >= 0)
+        a = set(int(x) for x in approx[t] if x >= 0)
+        out[t] = len(a & e) / len(e) if e else 1.0
+    return out
