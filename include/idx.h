@@ -1,0 +1,182 @@
+/* Causal lightning-indexer library for AMD Instinct MI355X (gfx950): C ABI.
+ *
+ * What the library computes (cited by page title and section):
+ *
+ *  - "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention",
+ *    Abstract: the indexer of token-level sparse attention scores every
+ *    preceding token of each query and keeps a per-query top-k; PIVOT groups
+ *    nearby queries, aggregates each group into one proxy query, runs one
+ *    shared full-prefix scan to a candidate set, then either re-scores the
+ *    candidates with each member's own indexer and keeps each member's own
+ *    top-k (Refine) or shares the proxy's top-k with the group (Reuse).
+ *    Groups are fixed-size runs of consecutive queries in prefill and the
+ *    queries of one multi-token-prediction step in decode.
+ *  - "ADIndex Restructures Sparse-Attention Indexing with Group-Level
+ *    Distillation", "Why the Indexer Becomes the Bottleneck": in prefill all
+ *    queries re-scan the same prefix; in decode each new query scans the
+ *    whole cached key history.  "Deployment Guidance": the full scan is kept
+ *    as the fallback path (idx_score_topk).
+ *  - "MLI Restructures DeepSeek Sparse Attention ...", "Core Idea": the
+ *    indexer keeps k = 2048 positions per query.
+ *
+ * Score (no page prints it; the DeepSeek lightning-indexer form is the
+ * reading):  I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]),  s <= pos(t),
+ * with pos(t) = q_pos0 + t.  For FP8 storage the real values are
+ * code * per-token scale.  Top-k order: score descending, then key index
+ * ascending (exact equality is a tie; -0 equals +0).  Rows with fewer
+ * eligible keys than k are filled with all of them and padded with -1.
+ * Each output row is a set: the order of its entries is unspecified.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named q, k, w, scales, out_*, cand, proxy_topk and ws are DEVICE
+ *    pointers to contiguous row-major buffers owned by the caller; the
+ *    idx_problem struct itself is a HOST pointer.  The library never
+ *    allocates or frees device memory and never synchronizes: all work is
+ *    enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ *  - Errors: every check is made on the host before anything is enqueued,
+ *    and on error nothing is enqueued.  IDX_EINVAL: a null required pointer,
+ *    a non-positive size, q_pos0 < 0 or q_pos0 + n_q > n_k, topk/group/n_cand
+ *    < 1, a scale pointer present for non-FP8 storage or missing for FP8.
+ *    IDX_EUNSUPPORTED: a (heads, dim, q dtype, k dtype) combination without a
+ *    kernel (supported: heads in {16, 32, 64}, dim in {64, 128}; dtypes
+ *    (F32, F32), (BF16, BF16), (BF16, FP8_E4M3), (FP8_E4M3, FP8_E4M3)).
+ *    IDX_EWORKSPACE: ws_bytes smaller than idx_workspace_bytes() reports as
+ *    the minimum.  IDX_EHIP: a HIP launch error (hipGetLastError).
+ *    Device-side faults surface at the caller's next synchronization; after
+ *    any error the outputs are undefined.
+ *  - Preconditions that are not checked: finite inputs, scales > 0, no
+ *    aliasing between outputs and inputs, n_k < 2^31.  Calls on distinct
+ *    workspaces are independent; two calls that share a workspace must be
+ *    ordered on one stream.
+ */
+#ifndef SATC_IDX_H
+#define SATC_IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats.  IDX_FP8_E4M3 is the OCP FP8 E4M3 format ("e4m3fn":
+ * bias 7, no infinities, max 448) with one float32 scale per token. */
+enum { IDX_F32 = 0, IDX_BF16 = 1, IDX_FP8_E4M3 = 2 };
+
+enum {
+  IDX_OK = 0,
+  IDX_EINVAL = -1,
+  IDX_EUNSUPPORTED = -2,
+  IDX_EWORKSPACE = -3,
+  IDX_EHIP = -4
+};
+
+/* Operation codes for idx_workspace_bytes. */
+enum {
+  IDX_OP_SCORE_TOPK = 0,
+  IDX_OP_GROUP_PROXY_SCAN = 1,
+  IDX_OP_REFINE_TOPK = 2,
+  IDX_OP_REUSE_TOPK = 3
+};
+
+/* One indexer problem: B sequences, each with n_q queries and n_k keys.
+ *   q       [B, n_q, heads, dim]  q_dtype   (dim fastest)
+ *   q_scale [B, n_q] float32, per query token (FP8 q only, else NULL)
+ *   k       [B, n_k, dim]         k_dtype
+ *   k_scale [B, n_k] float32, per key token (FP8 k only, else NULL)
+ *   w       [B, n_q, heads] float32 head weights
+ * Query t of a sequence sits at position pos(t) = q_pos0 + t of its key
+ * sequence: q_pos0 = 0 in prefill (n_q = n_k), n_k - n_q in decode (the key
+ * cache already holds the new tokens' keys). */
+typedef struct {
+  int32_t batch, n_q, n_k, q_pos0, heads, dim;
+  int32_t q_dtype, k_dtype;
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  const float* k_scale;
+  const float* w;
+} idx_problem;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t idx_version(void);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* idx_status_string(int32_t status);
+
+/* Workspace size in bytes that the operation `op` needs for problem `p`
+ * (group/n_cand/topk as the call will pass them; ignored where unused).
+ * Returns 0 when the operation needs none (or on invalid arguments).  Passing
+ * a larger workspace is allowed. */
+size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group,
+                           int32_t n_cand, int32_t topk);
+
+/* Dense causal indexer ("full-scan" path; PIVOT, Abstract: score every
+ * preceding token and keep each query's top-k).
+ *   out_idx    [B, n_q, topk] int32: the top min(topk, pos(t)+1) key
+ *              indices of each query, padded with -1.
+ *   out_scores optional [B, n_q, n_k] float32: the exact scores the select
+ *              used; positions beyond pos(t) are -inf.  NULL in timed runs.
+ * ws/ws_bytes: workspace of at least idx_workspace_bytes(p, IDX_OP_SCORE_TOPK,
+ * 0, 0, topk) bytes (may be NULL when that is 0). */
+int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx,
+                       float* out_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* PIVOT proxy and shared scan (PIVOT, Abstract: aggregate a group into one
+ * proxy query and run one shared full-prefix scan to a candidate set).
+ * Groups are runs of `group` consecutive queries of one sequence (the last
+ * may be shorter); n_g = ceil(n_q / group).  The proxy is the mean of the
+ * members' real q and of their w (float32 arithmetic), stored as bfloat16
+ * (round to nearest even) for BF16/FP8 q and as float32 for F32 q; FP8 keys
+ * are widened to bfloat16 (exactly) for the scan.  The scan of group g
+ * covers keys 0..pos(last member of g).
+ *   out_cand         [B, n_g, n_cand] int32: the top min(n_cand, prefix)
+ *                    keys of the proxy, padded with -1.  With
+ *                    n_cand = topk this is the Reuse input.
+ *   out_proxy_q      optional [B, n_g, heads, dim] (bfloat16 or float32).
+ *   out_proxy_w      optional [B, n_g, heads] float32.
+ *   out_proxy_scores optional [B, n_g, n_k] float32, -inf beyond the prefix. */
+int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand,
+                             int32_t* out_cand, void* out_proxy_q, float* out_proxy_w,
+                             float* out_proxy_scores, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* PIVOT-Refine (PIVOT, Abstract: re-score the candidate set with each
+ * query's own indexer and select an individual top-k).  Member t of group g
+ * considers V_t = { c in cand[b, g, :] : 0 <= c <= pos(t) } (entries outside
+ * [0, n_k) are empty slots) and keeps its top min(topk, |V_t|).  Candidate
+ * entries of one row must be distinct.
+ *   cand            [B, n_g, n_cand] int32 (e.g. out_cand of the proxy scan).
+ *   out_idx         [B, n_q, topk] int32, padded with -1.
+ *   out_cand_scores optional [B, n_q, n_cand] float32, -inf for excluded slots. */
+int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand,
+                        int32_t n_cand, int32_t topk, int32_t* out_idx,
+                        float* out_cand_scores, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* PIVOT-Reuse (PIVOT, Abstract: share the proxy top-k across the group).
+ * Member t of group g keeps { c in proxy_topk[b, g, :] : 0 <= c <= pos(t) }
+ * in the proxy's order, padded with -1 (no refill).  Integer only; only
+ * p->batch, n_q, n_k, q_pos0 are read (q/k/w may be NULL).
+ *   proxy_topk [B, n_g, topk] int32, out_idx [B, n_q, topk] int32. */
+int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy_topk,
+                       int32_t topk, int32_t* out_idx, void* stream);
+
+/* Kernel timing (measurement aid, off by default).  While enabled, every
+ * kernel the library enqueues is bracketed by a pair of HIP events recorded
+ * on the same stream; idx_profile_read synchronizes on the recorded events
+ * and reports, per kernel kind, the summed duration in milliseconds and the
+ * number of launches since the last read (then clears the records).
+ * Kinds: 0 score (MFMA scan), 1 select (top-k), 2 proxy build, 3 reuse,
+ * 4 fill (debug score dumps).  Returns IDX_EHIP on an event error.  Not
+ * reentrant: enable it from one host thread only. */
+enum { IDX_KERNEL_SCORE = 0, IDX_KERNEL_SELECT = 1, IDX_KERNEL_PROXY = 2, IDX_KERNEL_REUSE = 3,
+       IDX_KERNEL_FILL = 4, IDX_KERNEL_KINDS = 5 };
+int32_t idx_profile_enable(int32_t on);
+int32_t idx_profile_read(float* ms /* [IDX_KERNEL_KINDS] */, int32_t* launches /* [IDX_KERNEL_KINDS] */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SATC_IDX_H */

@@ -1,0 +1,224 @@
+"""Causal lightning indexer and PIVOT group-shared indexing on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in ``include/idx.h``: it checks
+tensor shapes and devices, allocates outputs and workspace with torch, and
+passes raw device pointers and the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no other path, and
+the functions raise if the library has not been built.
+
+Entry points (same names as the C ABI):
+
+* ``score_topk``        dense causal scan + per-query top-k
+* ``group_proxy_scan``  PIVOT proxy per group + one shared prefix scan -> candidates
+* ``refine_topk``       PIVOT-Refine: per-query re-score of the group's candidates
+* ``reuse_topk``        PIVOT-Reuse: the group's shared top-k, causally filtered
+"""
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
+IDX_OP_SCORE_TOPK, IDX_OP_GROUP_PROXY_SCAN, IDX_OP_REFINE_TOPK, IDX_OP_REUSE_TOPK = 0, 1, 2, 3
+
+_DTYPES = {torch.float32: IDX_F32, torch.bfloat16: IDX_BF16, torch.float8_e4m3fn: IDX_FP8_E4M3}
+
+
+class IndexerError(RuntimeError):
+    pass
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("n_k", ctypes.c_int32),
+        ("q_pos0", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p),
+        ("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+        ("w", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path():
+    return LIB_PATH
+
+
+def load_library():
+    """Load the built HIP library (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise IndexerError(
+                f"HIP library {LIB_PATH} is not built; run "
+                "`python -m sparse_attention_token_causal_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(_Problem)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        lib.idx_version.restype = i32
+        lib.idx_status_string.restype = ctypes.c_char_p
+        lib.idx_status_string.argtypes = [i32]
+        lib.idx_workspace_bytes.restype = sz
+        lib.idx_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
+        lib.idx_score_topk.restype = i32
+        lib.idx_score_topk.argtypes = [P, i32, vp, vp, vp, sz, vp]
+        lib.idx_group_proxy_scan.restype = i32
+        lib.idx_group_proxy_scan.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        lib.idx_refine_topk.restype = i32
+        lib.idx_refine_topk.argtypes = [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]
+        lib.idx_reuse_topk.restype = i32
+        lib.idx_reuse_topk.argtypes = [P, i32, vp, i32, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc):
+    if rc != 0:
+        raise IndexerError(f"indexer call failed: {load_library().idx_status_string(rc).decode()} ({rc})")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise IndexerError("inputs must be contiguous tensors on the GPU")
+
+
+def make_problem(q, k, w, q_scale=None, k_scale=None, q_pos0=None):
+    """q [B, n_q, H, d], k [B, n_k, d], w [B, n_q, H] float32; scales float32 per token.
+
+    q_pos0 defaults to n_k - n_q (prefill when n_q == n_k, decode otherwise).
+    The returned struct keeps references to the tensors it points at.
+    """
+    if q.dim() != 4 or k.dim() != 3 or w.dim() != 3:
+        raise IndexerError("expected q [B,n_q,H,d], k [B,n_k,d], w [B,n_q,H]")
+    B, n_q, H, d = q.shape
+    if k.shape[0] != B or k.shape[2] != d or tuple(w.shape) != (B, n_q, H):
+        raise IndexerError("q/k/w shapes disagree")
+    if w.dtype != torch.float32:
+        raise IndexerError("w must be float32")
+    for s, n in ((q_scale, n_q), (k_scale, k.shape[1])):
+        if s is not None and (s.dtype != torch.float32 or tuple(s.shape) != (B, n)):
+            raise IndexerError("scales must be float32 [B, tokens]")
+    if q.dtype not in _DTYPES or k.dtype not in _DTYPES:
+        raise IndexerError(f"unsupported storage dtype {q.dtype}/{k.dtype}")
+    _need_gpu(q, k, w, q_scale, k_scale)
+    n_k = k.shape[1]
+    p = _Problem(B, n_q, n_k, n_k - n_q if q_pos0 is None else int(q_pos0), H, d,
+                 _DTYPES[q.dtype], _DTYPES[k.dtype], _ptr(q), _ptr(q_scale), _ptr(k),
+                 _ptr(k_scale), _ptr(w))
+    p._keep = (q, k, w, q_scale, k_scale)
+    return p
+
+
+def workspace_bytes(p, op, group=0, n_cand=0, topk=0):
+    return int(load_library().idx_workspace_bytes(ctypes.byref(p), op, group, n_cand, topk))
+
+
+def _workspace(p, op, device, group=0, n_cand=0, topk=0, workspace=None):
+    n = workspace_bytes(p, op, group, n_cand, topk)
+    if workspace is not None:
+        if workspace.numel() < n:
+            raise IndexerError(f"workspace has {workspace.numel()} bytes, needs {n}")
+        return workspace
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def score_topk(q, k, w, topk, q_scale=None, k_scale=None, q_pos0=None, return_scores=False,
+               workspace=None, out=None):
+    """Dense causal indexer top-k: int32 [B, n_q, topk] (-1 padded; row order unspecified).
+
+    With ``return_scores`` also returns the exact float32 [B, n_q, n_k] scores
+    the select used (-inf beyond each query's prefix).
+    """
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    B, n_q = q.shape[0], q.shape[1]
+    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=q.device)
+    scores = torch.empty((B, n_q, k.shape[1]), dtype=torch.float32, device=q.device) if return_scores else None
+    ws = _workspace(p, IDX_OP_SCORE_TOPK, q.device, topk=topk, workspace=workspace)
+    _check(lib.idx_score_topk(ctypes.byref(p), topk, _ptr(idx), _ptr(scores), _ptr(ws), ws.numel(),
+                              _stream(q.device)))
+    return (idx, scores) if return_scores else idx
+
+
+def group_proxy_scan(q, k, w, group, n_cand, q_scale=None, k_scale=None, q_pos0=None,
+                     return_proxy=False, return_scores=False, workspace=None):
+    """PIVOT proxy + shared scan: candidates int32 [B, n_g, n_cand] (-1 padded).
+
+    ``return_proxy`` adds the stored proxy (q as bfloat16, or float32 for
+    float32 q; w float32); ``return_scores`` adds the proxy scores [B, n_g, n_k].
+    """
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    B, n_q, H, d = q.shape
+    n_g = -(-n_q // group)
+    cand = torch.empty((B, n_g, n_cand), dtype=torch.int32, device=q.device)
+    pq = pw = ps = None
+    if return_proxy:
+        pq = torch.empty((B, n_g, H, d), dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
+                         device=q.device)
+        pw = torch.empty((B, n_g, H), dtype=torch.float32, device=q.device)
+    if return_scores:
+        ps = torch.empty((B, n_g, k.shape[1]), dtype=torch.float32, device=q.device)
+    ws = _workspace(p, IDX_OP_GROUP_PROXY_SCAN, q.device, group, n_cand, workspace=workspace)
+    _check(lib.idx_group_proxy_scan(ctypes.byref(p), group, n_cand, _ptr(cand), _ptr(pq), _ptr(pw),
+                                    _ptr(ps), _ptr(ws), ws.numel(), _stream(q.device)))
+    res = [cand]
+    if return_proxy:
+        res += [pq, pw]
+    if return_scores:
+        res.append(ps)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def refine_topk(q, k, w, cand, group, topk, q_scale=None, k_scale=None, q_pos0=None,
+                return_scores=False, workspace=None, out=None):
+    """PIVOT-Refine: int32 [B, n_q, topk]; optional per-candidate scores [B, n_q, n_cand]."""
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    B, n_q = q.shape[0], q.shape[1]
+    n_g = -(-n_q // group)
+    if cand.dtype != torch.int32 or cand.dim() != 3 or tuple(cand.shape[:2]) != (B, n_g):
+        raise IndexerError("cand must be int32 [B, n_g, n_cand]")
+    _need_gpu(cand)
+    n_cand = cand.shape[2]
+    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, n_q, n_cand), dtype=torch.float32, device=q.device) if return_scores else None
+    ws = _workspace(p, IDX_OP_REFINE_TOPK, q.device, group, n_cand, topk, workspace=workspace)
+    _check(lib.idx_refine_topk(ctypes.byref(p), group, _ptr(cand), n_cand, topk, _ptr(idx), _ptr(sc),
+                               _ptr(ws), ws.numel(), _stream(q.device)))
+    return (idx, sc) if return_scores else idx
+
+
+def reuse_topk(proxy_topk, group, n_q, n_k, q_pos0=None, out=None):
+    """PIVOT-Reuse: int32 [B, n_q, topk] from the proxy top-k [B, n_g, topk]."""
+    lib = load_library()
+    if proxy_topk.dtype != torch.int32 or proxy_topk.dim() != 3:
+        raise IndexerError("proxy_topk must be int32 [B, n_g, topk]")
+    _need_gpu(proxy_topk)
+    B, n_g, topk = proxy_topk.shape
+    if n_g != -(-n_q // group):
+        raise IndexerError("proxy_topk has the wrong number of groups")
+    p = _Problem(B, n_q, n_k, n_k - n_q if q_pos0 is None else int(q_pos0), 0, 0, 0, 0,
+                 None, None, None, None, None)
+    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=proxy_topk.device)
+    _check(lib.idx_reuse_topk(ctypes.byref(p), group, _ptr(proxy_topk), topk, _ptr(idx),
+                              _stream(proxy_topk.device)))
+    return idx
+
+
+__all__ = ["score_topk", "group_proxy_scan", "refine_topk", "reuse_topk", "make_problem",
+           "workspace_bytes", "load_library", "library_path", "IndexerError"]

@@ -1,0 +1,322 @@
+// C ABI of the indexer library: argument checks, workspace carving, kernel
+// dispatch.  Every check happens on the host before anything is enqueued.
+#include "idx.h"
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+using namespace idx;
+
+constexpr size_t kAlign = 256;
+constexpr size_t kScoreBufferTarget = size_t(1) << 30;  // score rows buffered per chunk (bytes)
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+bool dtype_ok(int d) { return d == IDX_F32 || d == IDX_BF16 || d == IDX_FP8_E4M3; }
+
+bool combo_supported(int qf, int kf, int H, int D) {
+  if (!(H == 16 || H == 32 || H == 64)) return false;
+  if (!(D == 64 || D == 128)) return false;
+  return (qf == IDX_F32 && kf == IDX_F32) || (qf == IDX_BF16 && kf == IDX_BF16) ||
+         (qf == IDX_BF16 && kf == IDX_FP8_E4M3) || (qf == IDX_FP8_E4M3 && kf == IDX_FP8_E4M3);
+}
+
+// Shape and pointer checks shared by the scoring entry points.
+int check_problem(const idx_problem* p) {
+  if (!p) return IDX_EINVAL;
+  if (p->batch < 1 || p->n_q < 1 || p->n_k < 1 || p->heads < 1 || p->dim < 1) return IDX_EINVAL;
+  if (p->q_pos0 < 0 || (long long)p->q_pos0 + p->n_q > p->n_k) return IDX_EINVAL;
+  if (!dtype_ok(p->q_dtype) || !dtype_ok(p->k_dtype)) return IDX_EINVAL;
+  if (!p->q || !p->k || !p->w) return IDX_EINVAL;
+  if ((p->q_dtype == IDX_FP8_E4M3) != (p->q_scale != nullptr)) return IDX_EINVAL;
+  if ((p->k_dtype == IDX_FP8_E4M3) != (p->k_scale != nullptr)) return IDX_EINVAL;
+  if (!combo_supported(p->q_dtype, p->k_dtype, p->heads, p->dim)) return IDX_EUNSUPPORTED;
+  return IDX_OK;
+}
+
+// Row-waves per score workgroup: enough 64-row waves for the rows of one
+// segment (a sequence or a group), a power of two in [2, 8].
+int pick_rw(long long rows_per_segment, int H) {
+  const long long waves = (rows_per_segment * H + 63) / 64;
+  int rw = 2;
+  while (rw < 8 && rw < waves) rw *= 2;
+  return rw;
+}
+
+int queries_per_block(int rw, int H) { return rw * (64 / H); }
+
+// First flattened row covered by score block `blk` (blk == total -> end).
+long long block_start_row(int mode, int blk, int total, int B, int n_rows, int n_q, int group,
+                          int BQ) {
+  if (blk >= total) return (long long)B * (mode == kModeGather ? n_q : n_rows);
+  if (mode != kModeGather) {
+    const int bps = ceil_div(n_rows, BQ);
+    const int b = blk / bps, r = (blk % bps) * BQ;
+    return (long long)b * n_rows + r;
+  }
+  const int n_g = ceil_div(n_q, group), bpg = ceil_div(group, BQ);
+  const int b = blk / (n_g * bpg), g = (blk / bpg) % n_g, j = blk % bpg;
+  const int gs = g * group, ge = (gs + group < n_q) ? gs + group : n_q;
+  int r = gs + j * BQ;
+  if (r > ge) r = ge;
+  return (long long)b * n_q + r;
+}
+
+struct Layout {
+  int mode, rw, BQ, total_blocks, n_rows, n_cols;
+};
+
+Layout make_layout(int mode, const idx_problem* p, int n_rows, int n_cols, int group) {
+  Layout L;
+  L.mode = mode;
+  L.n_rows = n_rows;
+  L.n_cols = n_cols;
+  if (mode == kModeGather) {
+    const int seg = group < p->n_q ? group : p->n_q;
+    L.rw = pick_rw(seg, p->heads);
+    L.BQ = queries_per_block(L.rw, p->heads);
+    L.total_blocks = p->batch * ceil_div(p->n_q, group) * ceil_div(group, L.BQ);
+  } else {
+    L.rw = pick_rw(n_rows, p->heads);
+    L.BQ = queries_per_block(L.rw, p->heads);
+    L.total_blocks = p->batch * ceil_div(n_rows, L.BQ);
+  }
+  return L;
+}
+
+// Rows of the score buffer the workspace should hold for this layout.
+long long buffer_rows(const Layout& L, long long total_rows) {
+  long long rows = (long long)(kScoreBufferTarget / ((size_t)L.n_cols * 4));
+  if (rows < L.BQ) rows = L.BQ;
+  const long long padded = (long long)L.total_blocks * L.BQ;
+  if (rows > padded) rows = padded;
+  if (rows > total_rows + L.BQ) rows = total_rows + L.BQ;
+  return (rows + L.BQ - 1) / L.BQ * L.BQ;
+}
+
+// Score the rows block-chunk by block-chunk into `buf` and select each row's
+// top-k into `out`.  `full` = buf holds every row (row stride n_cols).
+int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D, int B, int n_q,
+                     int group, float* buf, long long buf_rows, bool full, int topk, int* out,
+                     hipStream_t st) {
+  const int bpc = full ? L.total_blocks : (int)(buf_rows / L.BQ);
+  if (bpc < 1) return IDX_EWORKSPACE;
+  const int tw = (8 / L.rw) * 64;
+  for (int blk0 = 0; blk0 < L.total_blocks; blk0 += bpc) {
+    const int nb = (L.total_blocks - blk0 < bpc) ? L.total_blocks - blk0 : bpc;
+    const long long r0 = block_start_row(L.mode, blk0, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
+    const long long r1 = block_start_row(L.mode, blk0 + nb, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
+    if (r1 <= r0) continue;
+    int chunks = 1;
+    if (nb < 1024) chunks = ceil_div(2048, nb);
+    int kc = ceil_div(L.n_cols, chunks);
+    kc = ceil_div(kc, tw) * tw;
+    chunks = ceil_div(L.n_cols, kc);
+    sa.blk0 = blk0;
+    sa.n_blocks = nb;
+    sa.row0 = full ? 0 : r0;
+    sa.out = buf;
+    sa.ld = L.n_cols;
+    sa.kc = kc;
+    sa.rw = L.rw;
+    if (launch_score(sa, qf, kf, H, D, chunks, st) != hipSuccess) return IDX_EHIP;
+    SelectArgs se;
+    se.scores = buf + (full ? r0 * (long long)L.n_cols : 0);
+    se.ld = L.n_cols;
+    se.row0 = r0;
+    se.n_rows = (L.mode == kModeGather) ? n_q : L.n_rows;
+    se.n_cols = L.n_cols;
+    se.mode = L.mode;
+    se.q_pos0 = sa.q_pos0;
+    se.n_q = n_q;
+    se.group = group;
+    se.cand = sa.cand;
+    se.topk = topk;
+    se.out = out;
+    if (launch_select(se, (int)(r1 - r0), st) != hipSuccess) return IDX_EHIP;
+  }
+  return IDX_OK;
+}
+
+ScoreArgs base_args(const idx_problem* p) {
+  ScoreArgs a = {};
+  a.q = p->q;
+  a.q_scale = p->q_scale;
+  a.k = p->k;
+  a.k_scale = p->k_scale;
+  a.w = p->w;
+  a.n_rows = p->n_q;
+  a.n_k = p->n_k;
+  a.n_q = p->n_q;
+  a.q_pos0 = p->q_pos0;
+  a.group = 1;
+  a.n_cols = p->n_k;
+  a.cand = nullptr;
+  a.mode = kModeDense;
+  return a;
+}
+
+int proxy_q_dtype(const idx_problem* p) { return p->q_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
+
+size_t proxy_q_bytes(const idx_problem* p, int n_g) {
+  return (size_t)p->batch * n_g * p->heads * p->dim * (proxy_q_dtype(p) == IDX_F32 ? 4 : 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t idx_version(void) { return 100; }
+
+const char* idx_status_string(int32_t s) {
+  switch (s) {
+    case IDX_OK: return "ok";
+    case IDX_EINVAL: return "invalid argument";
+    case IDX_EUNSUPPORTED: return "unsupported heads/dim/dtype combination";
+    case IDX_EWORKSPACE: return "workspace too small";
+    case IDX_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int32_t n_cand,
+                           int32_t topk) {
+  (void)topk;
+  if (op == IDX_OP_REUSE_TOPK) return 0;
+  if (check_problem(p) != IDX_OK) return 0;
+  if (op == IDX_OP_SCORE_TOPK) {
+    Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
+    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * p->n_k * 4);
+  }
+  if (group < 1) return 0;
+  const int n_g = ceil_div(p->n_q, group);
+  if (op == IDX_OP_GROUP_PROXY_SCAN) {
+    Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
+    return align_up(proxy_q_bytes(p, n_g)) + align_up((size_t)p->batch * n_g * p->heads * 4) +
+           align_up((size_t)buffer_rows(L, (long long)p->batch * n_g) * p->n_k * 4);
+  }
+  if (op == IDX_OP_REFINE_TOPK) {
+    if (n_cand < 1) return 0;
+    Layout L = make_layout(kModeGather, p, p->n_q, n_cand, group);
+    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * n_cand * 4);
+  }
+  return 0;
+}
+
+int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, float* out_scores,
+                       void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  if (topk < 1 || !out_idx) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
+  float* buf;
+  long long rows;
+  const bool full = out_scores != nullptr;
+  if (full) {
+    buf = out_scores;
+    rows = (long long)p->batch * p->n_q;
+    if (launch_fill(out_scores, (size_t)rows * p->n_k, -__builtin_huge_valf(), st) != hipSuccess)
+      return IDX_EHIP;
+  } else {
+    const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
+    if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+    buf = (float*)ws;
+    rows = (long long)(ws_bytes / ((size_t)p->n_k * 4));
+  }
+  ScoreArgs sa = base_args(p);
+  return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
+                          buf, rows, full, topk, out_idx, st);
+}
+
+int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand,
+                             int32_t* out_cand, void* out_proxy_q, float* out_proxy_w,
+                             float* out_proxy_scores, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  if (group < 1 || n_cand < 1 || !out_cand) return IDX_EINVAL;
+  const int pqf = proxy_q_dtype(p);
+  if (!combo_supported(pqf, p->k_dtype, p->heads, p->dim)) return IDX_EUNSUPPORTED;
+  const size_t need = idx_workspace_bytes(p, IDX_OP_GROUP_PROXY_SCAN, group, n_cand, 0);
+  if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int n_g = ceil_div(p->n_q, group);
+  char* cur = (char*)ws;
+  void* pq = out_proxy_q ? out_proxy_q : (void*)cur;
+  cur += align_up(proxy_q_bytes(p, n_g));
+  float* pw = out_proxy_w ? out_proxy_w : (float*)cur;
+  cur += align_up((size_t)p->batch * n_g * p->heads * 4);
+  if (launch_proxy_build(p->q, p->q_scale, p->w, p->batch, p->n_q, p->heads, p->dim, p->q_dtype,
+                         group, pq, pw, st) != hipSuccess)
+    return IDX_EHIP;
+  Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
+  const bool full = out_proxy_scores != nullptr;
+  float* buf;
+  long long rows;
+  if (full) {
+    buf = out_proxy_scores;
+    rows = (long long)p->batch * n_g;
+    if (launch_fill(buf, (size_t)rows * p->n_k, -__builtin_huge_valf(), st) != hipSuccess)
+      return IDX_EHIP;
+  } else {
+    buf = (float*)cur;
+    rows = (long long)((ws_bytes - (size_t)(cur - (char*)ws)) / ((size_t)p->n_k * 4));
+  }
+  ScoreArgs sa = base_args(p);
+  sa.q = pq;
+  sa.q_scale = nullptr;
+  sa.w = pw;
+  sa.n_rows = n_g;
+  sa.group = group;
+  sa.mode = kModeProxy;
+  return score_and_select(sa, L, pqf, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, group, buf,
+                          rows, full, n_cand, out_cand, st);
+}
+
+int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand, int32_t n_cand,
+                        int32_t topk, int32_t* out_idx, float* out_cand_scores, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  if (group < 1 || n_cand < 1 || topk < 1 || !cand || !out_idx) return IDX_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  Layout L = make_layout(kModeGather, p, p->n_q, n_cand, group);
+  const bool full = out_cand_scores != nullptr;
+  float* buf;
+  long long rows;
+  if (full) {
+    buf = out_cand_scores;
+    rows = (long long)p->batch * p->n_q;
+  } else {
+    const size_t need = idx_workspace_bytes(p, IDX_OP_REFINE_TOPK, group, n_cand, topk);
+    if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+    buf = (float*)ws;
+    rows = (long long)(ws_bytes / ((size_t)n_cand * 4));
+  }
+  ScoreArgs sa = base_args(p);
+  sa.group = group;
+  sa.n_cols = n_cand;
+  sa.cand = cand;
+  sa.mode = kModeGather;
+  return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q,
+                          group, buf, rows, full, topk, out_idx, st);
+}
+
+int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy_topk,
+                       int32_t topk, int32_t* out_idx, void* stream) {
+  if (!p || p->batch < 1 || p->n_q < 1 || p->n_k < 1) return IDX_EINVAL;
+  if (p->q_pos0 < 0 || (long long)p->q_pos0 + p->n_q > p->n_k) return IDX_EINVAL;
+  if (group < 1 || topk < 1 || !proxy_topk || !out_idx) return IDX_EINVAL;
+  if (launch_reuse(proxy_topk, p->batch, p->n_q, p->q_pos0, group, topk, out_idx,
+                   (hipStream_t)stream) != hipSuccess)
+    return IDX_EHIP;
+  return IDX_OK;
+}
+
+}  // extern "C"

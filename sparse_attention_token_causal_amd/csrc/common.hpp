@@ -1,0 +1,79 @@
+// Device-side building blocks shared by the indexer kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+enum Fmt : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kWave = 64;
+
+// Order-preserving map float -> uint32 (larger float -> larger key).  -0 is
+// canonicalised to +0 first so that the two compare equal, as the tie rule
+// requires.  Every finite value maps above kKeyExcluded, which marks an
+// entry that is not eligible (masked).
+constexpr uint32_t kKeyExcluded = 0u;
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float neg_inf() { return __uint_as_float(0xFF800000u); }
+
+// bfloat16 bits of an exactly representable float (truncation is exact when
+// the low 16 bits are zero, as for every widened FP8 E4M3 value).
+__device__ __forceinline__ uint32_t bf16_hi(float f) { return __float_as_uint(f) >> 16; }
+
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Four OCP E4M3 codes (one dword) -> four bfloat16 values packed in two
+// dwords (low code first).  The hardware conversion yields exact float32
+// values; E4M3 has 3 mantissa bits, so the bfloat16 truncation is exact.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t codes, uint32_t& lo, uint32_t& hi) {
+  auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);  // codes 0,1
+  auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);   // codes 2,3
+  lo = bf16_hi(a[0]) | (bf16_hi(a[1]) << 16);
+  hi = bf16_hi(b[0]) | (bf16_hi(b[1]) << 16);
+}
+
+__device__ __forceinline__ float fp8_to_f32(uint32_t code) {
+  auto a = __builtin_amdgcn_cvt_pk_f32_fp8(code & 0xFFu, false);
+  return a[0];
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, kWave); }
+
+// Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(v, off, kWave);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace idx

@@ -1,0 +1,102 @@
+// PIVOT proxy construction and Reuse broadcast for gfx950.
+//
+// "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention",
+// Abstract: a group of nearby queries is aggregated into a single proxy
+// query (read here as the mean of the members' real q and of their head
+// weights w); PIVOT-Reuse shares the proxy's top-k with every member.  A
+// member keeps only the shared entries inside its own causal prefix and the
+// freed slots are not refilled.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace idx {
+
+// One workgroup per (group, sequence).  Sums run over the members in token
+// order in float32, then divide by the member count; the proxy q is stored
+// as bfloat16 (nearest, ties to even) for BF16/FP8 inputs and as float32 for
+// F32 inputs, the proxy w as float32.  HBM-bound: every q element is read
+// once, coalesced along (head, dim).
+template <int QF>
+__global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const float* q_scale,
+                                                          const float* w, int n_q, int H, int D,
+                                                          int group, void* pq, float* pw) {
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int n_g = (n_q + group - 1) / group;
+  const int t0 = g * group, t1 = min(t0 + group, n_q);
+  const float n = (float)(t1 - t0);
+  const size_t HD = (size_t)H * D;
+  const size_t prow = (size_t)b * n_g + g;
+  for (size_t e = threadIdx.x; e < HD; e += blockDim.x) {
+    float s = 0.f;
+    for (int t = t0; t < t1; ++t) {
+      const size_t off = ((size_t)b * n_q + t) * HD + e;
+      float v;
+      if (QF == F32) {
+        v = ((const float*)q)[off];
+      } else if (QF == BF16) {
+        v = __uint_as_float((uint32_t)((const uint16_t*)q)[off] << 16);
+      } else {
+        v = fp8_to_f32(((const uint8_t*)q)[off]) * q_scale[(size_t)b * n_q + t];
+      }
+      s += v;
+    }
+    const float m = s / n;
+    if (QF == F32)
+      ((float*)pq)[prow * HD + e] = m;
+    else
+      ((uint16_t*)pq)[prow * HD + e] = f32_to_bf16_rne(m);
+  }
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float s = 0.f;
+    for (int t = t0; t < t1; ++t) s += w[((size_t)b * n_q + t) * H + h];
+    pw[prow * H + h] = s / n;
+  }
+}
+
+hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* w, int B, int n_q,
+                              int H, int D, int qf, int group, void* pq, float* pw,
+                              hipStream_t st) {
+  const int n_g = (n_q + group - 1) / group;
+  dim3 grid(n_g, B);
+  if (qf == F32)
+    hipLaunchKernelGGL(proxy_build_kernel<F32>, grid, dim3(256), 0, st, q, q_scale, w, n_q, H, D, group, pq, pw);
+  else if (qf == BF16)
+    hipLaunchKernelGGL(proxy_build_kernel<BF16>, grid, dim3(256), 0, st, q, q_scale, w, n_q, H, D, group, pq, pw);
+  else
+    hipLaunchKernelGGL(proxy_build_kernel<FP8>, grid, dim3(256), 0, st, q, q_scale, w, n_q, H, D, group, pq, pw);
+  return hipGetLastError();
+}
+
+// One wave per query: filter the group's shared list to the query's causal
+// prefix and compact it in order (ballot + popcount prefix), then pad.
+// HBM-write-bound: every member writes a full row of topk indices.
+__global__ __launch_bounds__(256) void reuse_kernel(const int* ptop, int n_q, int q_pos0, int group,
+                                                    int topk, int* out) {
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * (256 / kWave) + wave, b = blockIdx.y;
+  if (t >= n_q) return;
+  const int n_g = (n_q + group - 1) / group;
+  const int* src = ptop + ((size_t)b * n_g + t / group) * topk;
+  int* dst = out + ((size_t)b * n_q + t) * topk;
+  const int pos = q_pos0 + t;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int base = 0;
+  for (int c0 = 0; c0 < topk; c0 += kWave) {
+    const int c = c0 + lane;
+    const int v = c < topk ? src[c] : -1;
+    const bool keep = v >= 0 && v <= pos;
+    const unsigned long long m = __ballot(keep);
+    if (keep) dst[base + __popcll(m & lt)] = v;
+    base += __popcll(m);
+  }
+  for (int i = base + lane; i < topk; i += kWave) dst[i] = -1;
+}
+
+hipError_t launch_reuse(const int* ptop, int B, int n_q, int q_pos0, int group, int topk,
+                        int* out, hipStream_t st) {
+  dim3 grid((n_q + 3) / 4, B);
+  hipLaunchKernelGGL(reuse_kernel, grid, dim3(256), 0, st, ptop, n_q, q_pos0, group, topk, out);
+  return hipGetLastError();
+}
+
+}  // namespace idx

@@ -1,0 +1,295 @@
+// Causal indexer score kernel for gfx950.
+//
+// Computes I[t, s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]) for a block of
+// rows (queries, or PIVOT proxies) against a range of key columns.  The key
+// columns are either the positions 0..n_k-1 of the sequence (dense scan and
+// proxy scan) or a per-group candidate list (PIVOT-Refine re-score, keys
+// gathered by index).  Sources: "PIVOT: Efficient Query-Group Indexing for
+// Token-Level Sparse Attention", Abstract (score every preceding token; one
+// shared proxy scan; re-score the candidates per query); "ADIndex ...",
+// "Why the Indexer Becomes the Bottleneck" (whole causal prefix per query).
+//
+// Contraction on MFMA: rows = (query, head) pairs, columns = keys, inner
+// dimension = the head dimension d.  A wave owns 64 rows (two 32-row MFMA
+// blocks = 64/H queries) with its q fragments resident in registers, and 64
+// key columns per step (two 32-column blocks).  The 32x32 MFMA result layout
+// puts 16 rows of one column in each lane (row = 8*(v/4) + 4*(lane/32) + v%4,
+// column = lane%32), so the head reduction is an in-lane weighted sum plus
+// one exchange with lane^32.  The epilogue (ReLU, x w, sum over heads,
+// per-token FP8 scales, causal mask) runs on those registers; only the
+// per-(query, key) score leaves the wave.
+//
+// Key tiles are staged in LDS once per workgroup and read by every wave;
+// rows are padded by 16 bytes so that the 16-byte fragment reads of 16
+// consecutive lanes hit distinct banks.  FP8 keys scanned with bfloat16
+// queries are widened to bfloat16 while staged (exact).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace idx {
+
+template <int QF, int KF>
+struct MfmaTraits;
+
+// float32 x float32: v_mfma_f32_32x32x2_f32, one element of k per lane half.
+template <>
+struct MfmaTraits<F32, F32> {
+  static constexpr int KSTEP = 2, KE = 4, GE = 4;
+  typedef float frag;
+  __device__ static frag load_a(const char* rowp, int ks, int half) {
+    return *(const float*)(rowp + (ks * 2 + half) * 4);
+  }
+  __device__ static frag load_b(const char* ldsrow, int ks, int half) {
+    return *(const float*)(ldsrow + (ks * 2 + half) * 4);
+  }
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// bfloat16 x bfloat16: v_mfma_f32_32x32x16_bf16, 8 consecutive k per lane half.
+struct MfmaBf16 {
+  static constexpr int KSTEP = 16, KE = 2;
+  typedef bf16x8 frag;
+  __device__ static frag load_a(const char* rowp, int ks, int half) {
+    return *(const bf16x8*)(rowp + (ks * 16 + 8 * half) * 2);
+  }
+  __device__ static frag load_b(const char* ldsrow, int ks, int half) {
+    return *(const bf16x8*)(ldsrow + (ks * 16 + 8 * half) * 2);
+  }
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct MfmaTraits<BF16, BF16> : MfmaBf16 {
+  static constexpr int GE = 2;
+};
+template <>
+struct MfmaTraits<BF16, FP8> : MfmaBf16 {
+  static constexpr int GE = 1;  // staged from FP8, widened to bfloat16 in LDS
+};
+
+// FP8 x FP8: v_mfma_f32_32x32x64_f8f6f4 (both operands E4M3), 32 consecutive k per lane half.
+template <>
+struct MfmaTraits<FP8, FP8> {
+  static constexpr int KSTEP = 64, KE = 1, GE = 1;
+  typedef i32x8 frag;
+  __device__ static frag load_a(const char* rowp, int ks, int half) {
+    const i32x4* p = (const i32x4*)(rowp + ks * 64 + 32 * half);
+    i32x4 x = p[0], y = p[1];
+    frag f = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return f;
+  }
+  __device__ static frag load_b(const char* ldsrow, int ks, int half) {
+    const i32x4* p = (const i32x4*)(ldsrow + ks * 64 + 32 * half);
+    i32x4 x = p[0], y = p[1];
+    frag f = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return f;
+  }
+  __device__ static f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ int row_limit(const ScoreArgs& a, int r) {
+  if (a.mode == kModeProxy) return a.q_pos0 + min((r + 1) * a.group, a.n_q) - 1;
+  return a.q_pos0 + r;
+}
+
+template <int QF, int KF, int H, int D>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
+  typedef MfmaTraits<QF, KF> M;
+  constexpr int NKS = D / M::KSTEP;
+  constexpr int ROWB = D * M::KE + 16;
+  constexpr int QW = 64 / H;                  // queries per wave
+  constexpr int NW = kScoreThreads / kWave;   // 8 waves
+  constexpr bool WIDEN = (KF == FP8 && QF == BF16);
+  constexpr int CPC = D * M::GE / 16;         // 16-byte global chunks per key row
+
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int RW = a.rw, KW = NW / RW, TW = KW * 64;
+  char* ktile = smem;
+  int* colkey = (int*)(smem + TW * ROWB);
+  float* colscale = (float*)(colkey + TW);
+
+  const int wave = threadIdx.x / kWave, l = lane_id(), half = l >> 5, l32 = l & 31;
+  const int rw = wave % RW, kw = wave / RW;
+  const int BQ = RW * QW;
+
+  // ---- which rows this workgroup owns (longest prefixes first) ----
+  const int bid = a.blk0 + (a.n_blocks - 1 - (int)blockIdx.x);
+  int b, r_begin, r_end, g = 0;
+  if (a.mode != kModeGather) {
+    const int bps = (a.n_rows + BQ - 1) / BQ;
+    b = bid / bps;
+    r_begin = (bid % bps) * BQ;
+    r_end = min(r_begin + BQ, a.n_rows);
+  } else {
+    const int n_g = (a.n_q + a.group - 1) / a.group;
+    const int bpg = (a.group + BQ - 1) / BQ;
+    b = bid / (n_g * bpg);
+    g = (bid / bpg) % n_g;
+    const int gs = g * a.group, ge = min(gs + a.group, a.n_q);
+    r_begin = gs + (bid % bpg) * BQ;
+    r_end = min(r_begin + BQ, ge);
+    if (r_begin >= r_end) return;
+  }
+  int c_begin = (int)blockIdx.y * a.kc;
+  int c_end = min(c_begin + a.kc, a.n_cols);
+  if (a.mode != kModeGather) c_end = min(c_end, row_limit(a, r_end - 1) + 1);
+  if (c_begin >= c_end) return;
+
+  // ---- resident q fragments and head weights of this wave's 64 rows ----
+  const int t_first = r_begin + rw * QW;
+  typename M::frag afrag[2][NKS];
+  float wreg[2][16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int i = 32 * rb + l32;  // A-operand row of this lane
+    const int t = t_first + i / H, h = i % H;
+    const bool ok = t < r_end;
+    const char* rowp = (const char*)a.q + (((size_t)b * a.n_rows + (ok ? t : r_begin)) * H + h) * (size_t)D * (QF == F32 ? 4 : (QF == BF16 ? 2 : 1));
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      typename M::frag f = M::load_a(rowp, ks, half);
+      if (!ok) f = typename M::frag{};
+      afrag[rb][ks] = f;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ri = 32 * rb + 8 * (v / 4) + 4 * half + (v % 4);  // C-result row of register v
+      const int tt = t_first + ri / H, hh = ri % H;
+      float wv = 0.f;
+      if (tt < r_end) {
+        const size_t fr = (size_t)b * a.n_rows + tt;
+        wv = a.w[fr * H + hh];
+        if (QF == FP8) wv *= a.q_scale[fr];
+      }
+      wreg[rb][v] = wv;
+    }
+  }
+
+  const int n_g_all = (a.mode == kModeGather) ? (a.n_q + a.group - 1) / a.group : 0;
+  const int* cand_row = (a.mode == kModeGather) ? a.cand + ((size_t)b * n_g_all + g) * a.n_cols : nullptr;
+  const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * M::GE;
+
+  for (int c0 = c_begin; c0 < c_end; c0 += TW) {
+    // ---- stage the key tile (TW columns) in LDS ----
+    for (int i = threadIdx.x; i < TW * CPC; i += kScoreThreads) {
+      const int j = i / CPC, c = i % CPC;
+      const int col = c0 + j;
+      int s = -1;
+      if (col < c_end) s = (a.mode == kModeGather) ? cand_row[col] : col;
+      const bool ok = (s >= 0 && s < a.n_k);
+      i32x4 v = {0, 0, 0, 0};
+      if (ok) v = *(const i32x4*)(kseq + ((size_t)s * D * M::GE) + c * 16);
+      if (WIDEN) {
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4((uint32_t)v[e], o[2 * e], o[2 * e + 1]);
+        i32x4* dst = (i32x4*)(ktile + j * ROWB + c * 32);
+        dst[0] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+        dst[1] = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      } else {
+        *(i32x4*)(ktile + j * ROWB + c * 16) = v;
+      }
+      if (c == 0) {
+        colkey[j] = ok ? s : -1;
+        colscale[j] = (ok && KF == FP8) ? a.k_scale[(size_t)b * a.n_k + s] : 1.f;
+      }
+    }
+    __syncthreads();
+
+    // ---- MFMA: 2 row blocks x 2 column blocks over d ----
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const char* ldsrow = ktile + (kw * 64 + cb * 32 + l32) * ROWB;
+        typename M::frag bf = M::load_b(ldsrow, ks, half);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = M::mma(afrag[rb][ks], bf, acc[rb][cb]);
+      }
+    }
+
+    // ---- epilogue: ReLU, x w, sum over heads, scale, mask, store ----
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      float tot[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        float p = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if ((32 * rb + 8 * (v / 4)) / H == qi) p += wreg[rb][v] * fmaxf(acc[rb][cb][v], 0.f);
+        tot[cb] = p + xor32(p);
+      }
+      const int t = t_first + qi;
+      const int jl = kw * 64 + half * 32 + l32;  // lanes 0-31 store column block 0, 32-63 block 1
+      const int col = c0 + jl;
+      if (t < r_end && col < c_end) {
+        const int s = colkey[jl];
+        const bool ok = s >= 0 && s <= row_limit(a, t);
+        const float val = ok ? tot[half] * colscale[jl] : neg_inf();
+        a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int QF, int KF, int H, int D>
+static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((score_kernel<QF, KF, H, D>), grid, dim3(kScoreThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int QF, int KF, int H>
+static hipError_t pick_d(const ScoreArgs& a, int D, dim3 grid, size_t lds, hipStream_t st) {
+  if (D == 64) return launch_one<QF, KF, H, 64>(a, grid, lds, st);
+  if (D == 128) return launch_one<QF, KF, H, 128>(a, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+template <int QF, int KF>
+static hipError_t pick_h(const ScoreArgs& a, int H, int D, dim3 grid, size_t lds, hipStream_t st) {
+  if (H == 16) return pick_d<QF, KF, 16>(a, D, grid, lds, st);
+  if (H == 32) return pick_d<QF, KF, 32>(a, D, grid, lds, st);
+  if (H == 64) return pick_d<QF, KF, 64>(a, D, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+size_t score_lds_bytes(int qf, int kf, int D, int rw) {
+  const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
+  const int tw = (kScoreThreads / kWave / rw) * 64;
+  (void)kf;
+  return (size_t)tw * (D * ke + 16) + (size_t)tw * 8;
+}
+
+hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
+                        hipStream_t st) {
+  dim3 grid(a.n_blocks, n_col_chunks);
+  const size_t lds = score_lds_bytes(qf, kf, D, a.rw);
+  if (qf == F32 && kf == F32) return pick_h<F32, F32>(a, H, D, grid, lds, st);
+  if (qf == BF16 && kf == BF16) return pick_h<BF16, BF16>(a, H, D, grid, lds, st);
+  if (qf == BF16 && kf == FP8) return pick_h<BF16, FP8>(a, H, D, grid, lds, st);
+  if (qf == FP8 && kf == FP8) return pick_h<FP8, FP8>(a, H, D, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace idx

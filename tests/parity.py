@@ -1,0 +1,116 @@
+"""Shared helpers for the GPU-vs-oracle parity tests.
+
+Criteria (written here once, used by every parity test):
+
+* scores: |gpu - oracle| <= ATOL + RTOL * |oracle| per eligible entry, with
+  the oracle in float64 on the exact input bytes; excluded entries are -inf
+  on both sides;
+* select: the GPU's top-k set equals the oracle's select run on the GPU's
+  own float32 scores (bit-exact: same values, same tie rule);
+* set agreement against the oracle's own top-k, ignoring entries whose
+  oracle score lies within the score tolerance of the oracle's k-th score
+  (near-ties that float32 and float64 may order differently); required >=
+  AGREEMENT.
+"""
+
+import numpy as np
+import torch
+
+import oracle as O
+from sparse_attention_token_causal_amd import synth
+
+ATOL, RTOL = 1e-3, 2e-3
+AGREEMENT = 0.999
+
+
+def cuda():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    return torch.device("cuda:0")
+
+
+def real_inputs(inp):
+    """Decode the raw storage the GPU consumed into float64 (oracle side)."""
+    qs = None if inp["q_scale"] is None else inp["q_scale"].cpu().numpy()
+    ks = None if inp["k_scale"] is None else inp["k_scale"].cpu().numpy()
+    q = O.real_values(synth.raw_numpy(inp["q"]), synth.fmt_of(inp["q"]), qs)
+    k = O.real_values(synth.raw_numpy(inp["k"]), synth.fmt_of(inp["k"]), ks)
+    w = inp["w"].cpu().numpy().astype(np.float64)
+    return q, k, w
+
+
+def real_rows(inp, b, rows):
+    """Like real_inputs but only sequence b's listed query rows (for big workloads)."""
+    rows = torch.as_tensor(np.asarray(rows), device=inp["q"].device, dtype=torch.long)
+    qb = inp["q"][b].index_select(0, rows)
+    qs = None if inp["q_scale"] is None else inp["q_scale"][b].index_select(0, rows).cpu().numpy()
+    q = O.real_values(synth.raw_numpy(qb), synth.fmt_of(qb), qs)
+    w = inp["w"][b].index_select(0, rows).cpu().numpy().astype(np.float64)
+    ks = None if inp["k_scale"] is None else inp["k_scale"][b].cpu().numpy()
+    k = O.real_values(synth.raw_numpy(inp["k"][b]), synth.fmt_of(inp["k"]), ks)
+    return q, k, w
+
+
+def check_scores(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    m_ref = np.isneginf(ref)
+    assert np.array_equal(np.isneginf(gpu), m_ref), f"{what}: excluded entries differ"
+    e = ~m_ref
+    err = np.abs(gpu[e] - ref[e])
+    lim = ATOL + RTOL * np.abs(ref[e])
+    bad = err > lim
+    assert not bad.any(), (f"{what}: {bad.sum()} of {e.sum()} scores outside tolerance, "
+                           f"worst err/tol {np.max(err / lim):.3g}")
+    return float(np.max(err / lim)) if e.any() else 0.0
+
+
+def sets(rows):
+    return [frozenset(int(x) for x in r if x >= 0) for r in np.asarray(rows)]
+
+
+def assert_same_sets(a, b, what=""):
+    sa, sb = sets(a), sets(b)
+    bad = [i for i in range(len(sa)) if sa[i] != sb[i]]
+    assert not bad, f"{what}: {len(bad)} rows differ, first row {bad[0]}: " \
+                    f"only-a {sorted(sa[bad[0]] - sb[bad[0]])[:8]} only-b {sorted(sb[bad[0]] - sa[bad[0]])[:8]}"
+
+
+def check_rows_valid(idx, limits, topk, expect_counts=None):
+    """Distinct, causal, -1 padded at the end, and (optionally) the expected counts."""
+    idx = np.asarray(idx)
+    for t in range(idx.shape[0]):
+        row = idx[t]
+        n = int((row >= 0).sum())
+        assert (row[:n] >= 0).all() and (row[n:] == -1).all(), f"row {t}: padding not at the end"
+        assert len(set(row[:n].tolist())) == n, f"row {t}: duplicate indices"
+        assert (row[:n] <= limits[t]).all(), f"row {t}: index beyond the causal limit"
+        if expect_counts is not None:
+            assert n == expect_counts[t], f"row {t}: {n} entries, expected {expect_counts[t]}"
+
+
+def band_agreement(gpu_idx, ora_idx, ora_values, keys=None):
+    """1 - |symmetric difference outside the near-tie band| / (2 * sum k_eff).
+
+    ora_values[t] maps each eligible key of query t to its oracle score (an
+    array indexed by key when keys is None, else aligned with keys[t]).
+    """
+    num = 0
+    den = 0
+    for t in range(len(ora_idx)):
+        o = [int(x) for x in ora_idx[t] if x >= 0]
+        g = [int(x) for x in gpu_idx[t] if x >= 0]
+        den += 2 * len(o)
+        if not o:
+            continue
+        if keys is None:
+            val = lambda s: ora_values[t][s]
+        else:
+            lut = dict(zip((int(x) for x in keys[t]), ora_values[t]))
+            val = lambda s: lut[s]
+        tau = min(val(s) for s in o)
+        band = ATOL + RTOL * abs(tau)
+        for s in set(o) ^ set(g):
+            if abs(val(s) - tau) > band:
+                num += 1
+    return 1.0 - num / max(den, 1)

@@ -1,0 +1,114 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before touching the device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_token_causal_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "idx.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(idx_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return S.load_library()
+
+
+def test_header_declares_the_four_entry_points():
+    fns = declared_functions()
+    for f in ("idx_score_topk", "idx_group_proxy_scan", "idx_refine_topk", "idx_reuse_topk",
+              "idx_workspace_bytes", "idx_status_string", "idx_version"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+
+
+def test_status_strings(lib):
+    assert lib.idx_status_string(0) == b"ok"
+    assert b"workspace" in lib.idx_status_string(-3)
+    assert lib.idx_version() >= 100
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def problem(**kw):
+    d = dict(batch=1, n_q=64, n_k=64, q_pos0=0, heads=64, dim=128, q_dtype=1, k_dtype=1,
+             q=FAKE, q_scale=None, k=FAKE, k_scale=None, w=FAKE)
+    d.update(kw)
+    return S._Problem(d["batch"], d["n_q"], d["n_k"], d["q_pos0"], d["heads"], d["dim"],
+                      d["q_dtype"], d["k_dtype"], d["q"], d["q_scale"], d["k"], d["k_scale"], d["w"])
+
+
+def score(lib, p, topk=8, out=FAKE, ws=None, ws_bytes=0):
+    return lib.idx_score_topk(ctypes.byref(p), topk, out, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=0), dict(n_q=0), dict(n_k=0), dict(heads=0), dict(dim=0),
+    dict(q_pos0=-1), dict(n_q=65), dict(q_pos0=1), dict(q=None), dict(k=None), dict(w=None),
+    dict(q_dtype=7), dict(q_dtype=2),                   # fp8 q without its scale
+    dict(k_scale=FAKE),                                 # a scale for bf16 keys
+])
+def test_invalid_problem(lib, bad):
+    assert score(lib, problem(**bad)) == -1
+
+
+@pytest.mark.parametrize("bad", [dict(heads=8), dict(heads=128), dict(dim=96), dict(dim=256),
+                                 dict(q_dtype=0, k_dtype=1), dict(q_dtype=2, k_dtype=1, q_scale=FAKE)])
+def test_unsupported_combination(lib, bad):
+    assert score(lib, problem(**bad)) == -2
+
+
+def test_invalid_call_arguments(lib):
+    p = problem()
+    assert score(lib, p, topk=0) == -1
+    assert score(lib, p, out=None) == -1
+    assert lib.idx_group_proxy_scan(ctypes.byref(p), 0, 8, FAKE, None, None, None, None, 0, None) == -1
+    assert lib.idx_group_proxy_scan(ctypes.byref(p), 4, 0, FAKE, None, None, None, None, 0, None) == -1
+    assert lib.idx_refine_topk(ctypes.byref(p), 4, None, 8, 8, FAKE, None, None, 0, None) == -1
+    assert lib.idx_refine_topk(ctypes.byref(p), 4, FAKE, 8, 0, FAKE, None, None, 0, None) == -1
+    assert lib.idx_reuse_topk(ctypes.byref(p), 0, FAKE, 8, FAKE, None) == -1
+    assert lib.idx_reuse_topk(ctypes.byref(p), 4, None, 8, FAKE, None) == -1
+    assert lib.idx_reuse_topk(ctypes.byref(problem(n_q=65)), 4, FAKE, 8, FAKE, None) == -1
+
+
+def test_workspace_checks(lib):
+    p = problem()
+    need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 8)
+    assert need > 0
+    assert score(lib, p, ws=None, ws_bytes=0) == -3
+    assert score(lib, p, ws=FAKE, ws_bytes=need - 1) == -3
+    need_g = lib.idx_workspace_bytes(ctypes.byref(p), 1, 4, 16, 0)
+    assert lib.idx_group_proxy_scan(ctypes.byref(p), 4, 16, FAKE, None, None, None, FAKE,
+                                    need_g - 1, None) == -3
+    need_r = lib.idx_workspace_bytes(ctypes.byref(p), 2, 4, 16, 8)
+    assert lib.idx_refine_topk(ctypes.byref(p), 4, FAKE, 16, 8, FAKE, None, FAKE, need_r - 1, None) == -3
+    assert lib.idx_workspace_bytes(ctypes.byref(p), 3, 4, 16, 8) == 0
+
+
+def test_workspace_sizes_follow_the_layout(lib):
+    # dense: the score buffer holds whole rows of n_k float32, in whole row blocks
+    p = problem(n_q=1000, n_k=1000)
+    need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 8)
+    assert need >= 1000 * 1000 * 4 and need % 256 == 0
+    # large: capped near 1 GiB of buffered rows
+    big = problem(n_q=131072, n_k=131072)
+    nb = lib.idx_workspace_bytes(ctypes.byref(big), 0, 0, 0, 2048)
+    assert (1 << 30) <= nb <= (1 << 30) + 8 * 131072 * 4 + 256
+    # proxy scan: proxy q (bf16) + proxy w + score rows
+    g = lib.idx_workspace_bytes(ctypes.byref(p), 1, 10, 64, 0)
+    assert g >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + 100 * 1000 * 4

@@ -1,0 +1,196 @@
+"""GPU vs oracle parity on small workloads (every row checked), through the C ABI.
+
+Sizes span several key tiles and query blocks and end on ragged tails; the
+five storage/shape combinations of the kernels are all exercised, plus the
+degenerate cases (one token, k = 1, k above the prefix, group size 1, group
+larger than the sequence, decode positions).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_token_causal_amd as S
+from sparse_attention_token_causal_amd.synth import Workload, WORKLOADS, make_inputs
+
+from parity import (AGREEMENT, assert_same_sets, band_agreement, check_rows_valid, check_scores,
+                    cuda, real_inputs)
+
+pytestmark = pytest.mark.gpu
+
+DENSE = [
+    WORKLOADS["prefill_f32_L1024_H16_d64_k128"],
+    Workload("bf16_B2_L700_H64_d128", 2, 700, 700, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98, topk=128),
+    Workload("bf16_L333_H32_d64", 1, 333, 333, 32, 64, "bf16", "bf16", "normal8", "normal8", topk=50, seed=1),
+    Workload("f32_L200_H16_d128_k300", 1, 200, 200, 16, 128, "f32", "f32", "normal8", "normal8", topk=300, seed=2),
+    Workload("decode_bf16q_fp8k_B3", 3, 2, 5000, 64, 128, "bf16", "fp8", "ar1", "heavy", rho=0.98, topk=256, seed=3),
+    Workload("fp8_L600_H64_d128", 1, 600, 600, 64, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99, topk=100, seed=4),
+    Workload("decode_bf16_B2_nq4_H16_d64", 2, 4, 777, 16, 64, "bf16", "bf16", "normal8", "normal8", topk=33, seed=5),
+    Workload("f32_nq150_nk300_H64_d64", 1, 150, 300, 64, 64, "f32", "f32", "normal8", "heavy", topk=16, seed=6),
+    Workload("bf16_L1_k4", 1, 1, 1, 64, 128, "bf16", "bf16", "normal8", "normal8", topk=4, seed=7),
+    Workload("bf16_L90_k1", 1, 90, 90, 32, 128, "bf16", "bf16", "normal8", "heavy", topk=1, seed=8),
+]
+
+
+def args(inp, wl):
+    return dict(q_scale=inp["q_scale"], k_scale=inp["k_scale"], q_pos0=wl.q_pos0)
+
+
+@pytest.mark.parametrize("wl", DENSE, ids=[w.name for w in DENSE])
+def test_dense_parity(wl):
+    dev = cuda()
+    print(f"\n[dense] {wl.name}", flush=True)
+    inp = make_inputs(wl, dev)
+    idx, sc = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, return_scores=True, **args(inp, wl))
+    idx_ws = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **args(inp, wl))
+    torch.cuda.synchronize()
+    idx, sc, idx_ws = idx.cpu().numpy(), sc.cpu().numpy(), idx_ws.cpu().numpy()
+    # the timed path (workspace) and the dump path run the same kernels
+    assert np.array_equal(idx, idx_ws)
+    q, k, w = real_inputs(inp)
+    worst = 0.0
+    for b in range(wl.batch):
+        I = O.dense_scores(q[b], k[b], w[b], wl.q_pos0)
+        worst = max(worst, check_scores(sc[b], I, f"{wl.name} b={b}"))
+        # select on the GPU's own scores: bit-exact
+        own = _select_rows(sc[b], wl.q_pos0, wl.topk)
+        assert_same_sets(idx[b], own, f"{wl.name} b={b} select on own scores")
+        lim = wl.q_pos0 + np.arange(wl.n_q)
+        check_rows_valid(idx[b], lim, wl.topk, np.minimum(wl.topk, lim + 1))
+        ora = O.dense_topk(q[b], k[b], w[b], wl.q_pos0, wl.topk, scores=I)
+        agr = band_agreement(idx[b], ora, I)
+        assert agr >= AGREEMENT, f"{wl.name}: set agreement {agr}"
+    print(f"  worst err/tol {worst:.3g}", flush=True)
+
+
+def _select_rows(scores, q_pos0, topk):
+    rows = []
+    for t in range(scores.shape[0]):
+        p = q_pos0 + t
+        rows.append(O.select_topk(scores[t, : p + 1].astype(np.float64), np.arange(p + 1), topk))
+    out = np.full((scores.shape[0], topk), -1, dtype=np.int64)
+    for t, r in enumerate(rows):
+        out[t, : len(r)] = r
+    return out
+
+
+def test_dense_is_deterministic():
+    dev = cuda()
+    wl = DENSE[1]
+    inp = make_inputs(wl, dev)
+    a = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, return_scores=True, **args(inp, wl))
+    b = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, return_scores=True, **args(inp, wl))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+GROUPED = [
+    Workload("g_bf16_L777_G16_C200", 1, 777, 777, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98,
+             topk=64, group=16, n_cand=200, seed=11),
+    Workload("g_fp8_L500_G32_C150", 1, 500, 500, 64, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99,
+             topk=40, group=32, n_cand=150, seed=12),
+    Workload("g_f32_B2_L300_H16_d64_G5_C37", 2, 300, 300, 16, 64, "f32", "f32", "normal8", "normal8",
+             topk=11, group=5, n_cand=37, seed=13),
+    Workload("g_decode_bf16q_fp8k_B3_G2", 3, 2, 5000, 64, 128, "bf16", "fp8", "ar1", "heavy", rho=0.98,
+             topk=256, group=2, n_cand=512, seed=14),
+    Workload("g_bf16_L30_G100", 1, 30, 30, 32, 64, "bf16", "bf16", "normal8", "heavy", topk=8, group=100,
+             n_cand=12, seed=15),
+]
+
+
+@pytest.mark.parametrize("wl", GROUPED, ids=[w.name for w in GROUPED])
+def test_grouped_parity(wl):
+    dev = cuda()
+    print(f"\n[grouped] {wl.name}", flush=True)
+    inp = make_inputs(wl, dev)
+    a = args(inp, wl)
+    G, C, K = wl.group, wl.n_cand, wl.topk
+    cand, pq, pw, ps = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], G, C, return_proxy=True,
+                                          return_scores=True, **a)
+    ridx, rsc = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, G, K, return_scores=True, **a)
+    ridx_ws = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, G, K, **a)
+    cand_ws = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], G, C, **a)
+    ptop = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], G, K, **a)
+    uidx = S.reuse_topk(ptop, G, wl.n_q, wl.n_k, q_pos0=wl.q_pos0)
+    torch.cuda.synchronize()
+    assert torch.equal(ridx, ridx_ws) and torch.equal(cand, cand_ws)
+    q, k, w = real_inputs(inp)
+    pq_f = pq.float().cpu().numpy().astype(np.float64)
+    pw_f = pw.cpu().numpy().astype(np.float64)
+    cand, ps, ridx, rsc = cand.cpu().numpy(), ps.cpu().numpy(), ridx.cpu().numpy(), rsc.cpu().numpy()
+    ptop, uidx = ptop.cpu().numpy(), uidx.cpu().numpy()
+    n_g = -(-wl.n_q // G)
+    lim = O.proxy_limits(wl.n_q, G, wl.q_pos0)
+    for b in range(wl.batch):
+        # G1: the stored proxy is the rounded mean
+        qb, wb = O.proxy_means(q[b], w[b], G)
+        qr, wr = O.round_proxy(qb, wb, synth_fmt(wl))
+        if wl.q_fmt == "f32":
+            assert np.allclose(pq_f[b], qr, rtol=1e-6, atol=1e-7)
+        else:
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(qr), 1e-30))) - 7)
+            assert (np.abs(pq_f[b] - qr) <= ulp * 1.0001).all(), "proxy q beyond 1 bf16 ulp"
+        assert np.allclose(pw_f[b], wb, rtol=1e-6, atol=0)
+        # G2: proxy scores on the GPU's own proxy
+        P = O.proxy_scores(pq_f[b], pw_f[b], k[b], lim)
+        check_scores(ps[b], P, f"{wl.name} proxy scores b={b}")
+        # G3: candidates = oracle select on the GPU's proxy scores
+        own = O.proxy_candidates(ps[b].astype(np.float64), lim, C)
+        assert_same_sets(cand[b], own, f"{wl.name} candidates b={b}")
+        check_rows_valid(cand[b], lim, C, np.minimum(C, lim + 1))
+        # G4: refine scores per candidate slot
+        I = O.dense_scores(q[b], k[b], w[b], wl.q_pos0)
+        ref_sc = np.full((wl.n_q, C), -np.inf)
+        for t in range(wl.n_q):
+            c = cand[b, t // G]
+            ok = (c >= 0) & (c <= wl.q_pos0 + t)
+            ref_sc[t, ok] = I[t, c[ok]]
+        check_scores(rsc[b], ref_sc, f"{wl.name} refine scores b={b}")
+        # G5: refine select on the GPU's own scores
+        own = O.refine_topk(q[b], k[b], w[b], cand[b], G, wl.q_pos0, K, scores=rsc[b].astype(np.float64))
+        assert_same_sets(ridx[b], own, f"{wl.name} refine select b={b}")
+        check_rows_valid(ridx[b], wl.q_pos0 + np.arange(wl.n_q), K)
+        # G6: agreement with the oracle's refine on oracle scores
+        ora = O.refine_topk(q[b], k[b], w[b], cand[b], G, wl.q_pos0, K)
+        agr = band_agreement(ridx[b], ora, I)
+        assert agr >= AGREEMENT, f"{wl.name}: refine agreement {agr}"
+        # G7: reuse is integer work: exact, in the proxy's order
+        ora_u = O.reuse_topk(ptop[b], G, wl.q_pos0, wl.n_q, K)
+        assert np.array_equal(uidx[b], ora_u), f"{wl.name}: reuse differs"
+        assert n_g == cand.shape[1]
+
+
+def synth_fmt(wl):
+    return wl.q_fmt
+
+
+def test_group_size_one_matches_dense():
+    dev = cuda()
+    wl = Workload("g1_bf16_L300", 1, 300, 300, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98, topk=24,
+                  seed=21)
+    inp = make_inputs(wl, dev)
+    a = args(inp, wl)
+    dense = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **a)
+    ptop = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], 1, wl.topk, **a)
+    reuse = S.reuse_topk(ptop, 1, wl.n_q, wl.n_k, q_pos0=wl.q_pos0)
+    cand = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], 1, 100, **a)
+    refine = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, 1, wl.topk, **a)
+    torch.cuda.synchronize()
+    d, u, r = dense.cpu().numpy()[0], reuse.cpu().numpy()[0], refine.cpu().numpy()[0]
+    # a bf16 query is its own bf16 proxy, so the proxy scan is the dense scan
+    assert_same_sets(u, d, "reuse vs dense")
+    assert_same_sets(r, d, "refine vs dense")
+
+
+def test_refine_whole_prefix_equals_dense():
+    dev = cuda()
+    wl = Workload("wp_bf16_L256_G32", 1, 256, 256, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98,
+                  topk=20, seed=22)
+    inp = make_inputs(wl, dev)
+    a = args(inp, wl)
+    cand = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], 32, 256, **a)
+    refine = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, 32, wl.topk, **a)
+    dense = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **a)
+    torch.cuda.synchronize()
+    assert_same_sets(refine.cpu().numpy()[0], dense.cpu().numpy()[0], "refine(whole prefix) vs dense")
