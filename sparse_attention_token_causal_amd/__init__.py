@@ -19,7 +19,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsatc_idx.so")
 
 IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
 IDX_OP_SCORE_TOPK, IDX_OP_GROUP_PROXY_SCAN, IDX_OP_REFINE_TOPK, IDX_OP_REUSE_TOPK = 0, 1, 2, 3
@@ -73,6 +73,10 @@ def load_library():
         lib.idx_refine_topk.argtypes = [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]
         lib.idx_reuse_topk.restype = i32
         lib.idx_reuse_topk.argtypes = [P, i32, vp, i32, vp, vp]
+        lib.idx_profile_enable.restype = i32
+        lib.idx_profile_enable.argtypes = [i32]
+        lib.idx_profile_read.restype = i32
+        lib.idx_profile_read.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
         _lib = lib
     return _lib
 
@@ -220,5 +224,22 @@ def reuse_topk(proxy_topk, group, n_q, n_k, q_pos0=None, out=None):
     return idx
 
 
-__all__ = ["score_topk", "group_proxy_scan", "refine_topk", "reuse_topk", "make_problem",
+KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill")
+
+
+def profile_enable(on=True):
+    """Bracket every kernel the library enqueues with HIP events (measurement aid)."""
+    _check(load_library().idx_profile_enable(1 if on else 0))
+
+
+def profile_read():
+    """{kind: (total_ms, launches)} since the last read; synchronizes on the events."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_float * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(load_library().idx_profile_read(ms, cnt))
+    return {KERNEL_KINDS[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
+
+
+__all__ = ["profile_enable", "profile_read", "score_topk", "group_proxy_scan", "refine_topk", "reuse_topk", "make_problem",
            "workspace_bytes", "load_library", "library_path", "IndexerError"]

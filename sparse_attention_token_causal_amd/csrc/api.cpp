@@ -6,11 +6,47 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "kernels.hpp"
 
 namespace {
 
 using namespace idx;
+
+// ---- optional per-kernel timing with HIP events (measurement aid) ----
+struct TimedLaunch {
+  int kind;
+  hipEvent_t start, stop;
+};
+bool g_profile = false;
+std::vector<TimedLaunch> g_records;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (a callable returning hipError_t), bracketed by events when
+// profiling is on.
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F launch) {
+  if (!g_profile) return launch();
+  TimedLaunch r{kind, take_event(), take_event()};
+  if (!r.start || !r.stop) return hipErrorOutOfMemory;
+  hipEventRecord(r.start, st);
+  hipError_t e = launch();
+  hipEventRecord(r.stop, st);
+  g_records.push_back(r);
+  return e;
+}
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreBufferTarget = size_t(1) << 30;  // score rows buffered per chunk (bytes)
@@ -125,7 +161,8 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.ld = L.n_cols;
     sa.kc = kc;
     sa.rw = L.rw;
-    if (launch_score(sa, qf, kf, H, D, chunks, st) != hipSuccess) return IDX_EHIP;
+    if (timed(IDX_KERNEL_SCORE, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
+      return IDX_EHIP;
     SelectArgs se;
     se.scores = buf + (full ? r0 * (long long)L.n_cols : 0);
     se.ld = L.n_cols;
@@ -139,7 +176,8 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     se.cand = sa.cand;
     se.topk = topk;
     se.out = out;
-    if (launch_select(se, (int)(r1 - r0), st) != hipSuccess) return IDX_EHIP;
+    if (timed(IDX_KERNEL_SELECT, st, [&] { return launch_select(se, (int)(r1 - r0), st); }) != hipSuccess)
+      return IDX_EHIP;
   }
   return IDX_OK;
 }
@@ -222,7 +260,9 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
   if (full) {
     buf = out_scores;
     rows = (long long)p->batch * p->n_q;
-    if (launch_fill(out_scores, (size_t)rows * p->n_k, -__builtin_huge_valf(), st) != hipSuccess)
+    if (timed(IDX_KERNEL_FILL, st, [&] {
+          return launch_fill(out_scores, (size_t)rows * p->n_k, -__builtin_huge_valf(), st);
+        }) != hipSuccess)
       return IDX_EHIP;
   } else {
     const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
@@ -252,8 +292,10 @@ int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand
   cur += align_up(proxy_q_bytes(p, n_g));
   float* pw = out_proxy_w ? out_proxy_w : (float*)cur;
   cur += align_up((size_t)p->batch * n_g * p->heads * 4);
-  if (launch_proxy_build(p->q, p->q_scale, p->w, p->batch, p->n_q, p->heads, p->dim, p->q_dtype,
-                         group, pq, pw, st) != hipSuccess)
+  if (timed(IDX_KERNEL_PROXY, st, [&] {
+        return launch_proxy_build(p->q, p->q_scale, p->w, p->batch, p->n_q, p->heads, p->dim,
+                                  p->q_dtype, group, pq, pw, st);
+      }) != hipSuccess)
     return IDX_EHIP;
   Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
   const bool full = out_proxy_scores != nullptr;
@@ -262,7 +304,9 @@ int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand
   if (full) {
     buf = out_proxy_scores;
     rows = (long long)p->batch * n_g;
-    if (launch_fill(buf, (size_t)rows * p->n_k, -__builtin_huge_valf(), st) != hipSuccess)
+    if (timed(IDX_KERNEL_FILL, st, [&] {
+          return launch_fill(buf, (size_t)rows * p->n_k, -__builtin_huge_valf(), st);
+        }) != hipSuccess)
       return IDX_EHIP;
   } else {
     buf = (float*)cur;
@@ -313,10 +357,38 @@ int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy
   if (!p || p->batch < 1 || p->n_q < 1 || p->n_k < 1) return IDX_EINVAL;
   if (p->q_pos0 < 0 || (long long)p->q_pos0 + p->n_q > p->n_k) return IDX_EINVAL;
   if (group < 1 || topk < 1 || !proxy_topk || !out_idx) return IDX_EINVAL;
-  if (launch_reuse(proxy_topk, p->batch, p->n_q, p->q_pos0, group, topk, out_idx,
-                   (hipStream_t)stream) != hipSuccess)
+  hipStream_t st = (hipStream_t)stream;
+  if (timed(IDX_KERNEL_REUSE, st, [&] {
+        return launch_reuse(proxy_topk, p->batch, p->n_q, p->q_pos0, group, topk, out_idx, st);
+      }) != hipSuccess)
     return IDX_EHIP;
   return IDX_OK;
+}
+
+int32_t idx_profile_enable(int32_t on) {
+  g_profile = on != 0;
+  return IDX_OK;
+}
+
+int32_t idx_profile_read(float* ms, int32_t* launches) {
+  int rc = IDX_OK;
+  for (int i = 0; i < IDX_KERNEL_KINDS; ++i) {
+    if (ms) ms[i] = 0.f;
+    if (launches) launches[i] = 0;
+  }
+  for (const TimedLaunch& r : g_records) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess)
+      rc = IDX_EHIP;
+    if (r.kind >= 0 && r.kind < IDX_KERNEL_KINDS) {
+      if (ms) ms[r.kind] += t;
+      if (launches) launches[r.kind] += 1;
+    }
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_records.clear();
+  return rc;
 }
 
 }  // extern "C"
