@@ -6,81 +6,47 @@
 // Abstract: each query keeps its own top-k of the scanned or re-scored
 // keys; the tie rule is the reading given in the library header).
 //
-// Method: scores are mapped to order-preserving 32-bit keys; a most-
-// significant-digit-first radix select (four 8-bit digits) finds the key tau
-// of the k-th entry and how many entries equal to tau still belong to the
-// top-k.  If only part of the tie class is taken, a second radix select
-// (ascending, over the key indices of the tied entries) finds the largest
-// admitted index.  A final ordered compaction (wave ballot + popcount prefix
-// counts) writes the winners in column order and pads the row with -1.
-// Histograms live in LDS in eight copies (lane & 7) to spread same-bin
-// atomics; rows of up to 32768 keys are cached in LDS, longer rows are
-// re-read from global memory on each pass.
+// Method (scores are mapped to order-preserving 32-bit keys):
+//  1. load the row (into registers when it is short enough, coalesced) and
+//     reduce the count, minimum and maximum of the eligible keys;
+//  2. all eligible keys share the bits above the highest bit where min and
+//     max differ, so one 2048-bin histogram of the next 11 bits spreads the
+//     row; a suffix scan finds the bin b* holding the k-th key;
+//  3. every key in a bin above b* is a winner; the keys of b* are gathered
+//     into an LDS list and ranked exactly by counting how many list entries
+//     precede each one in (key desc, index asc) order; the first `need`
+//     ranks win (ties need no second pass: the index is part of the order);
+//     while the boundary bin is larger than the list, the histogram step is
+//     repeated on the next 11 bits inside it (an MSB-first radix descent); a
+//     class of equal keys larger than the list is split by an ascending radix
+//     select over the key indices;
+//  4. winners are written with one block-wide prefix scan of per-thread
+//     counts (the row is a set; the order is fixed by the thread layout),
+//     the boundary winners at their rank, and the row is padded with -1.
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace idx {
 
-constexpr int kCopies = 8;
-constexpr int kCopyStride = 257;
+constexpr int kBins = 2048;
+constexpr int kListCap = 2048;  // LDS list capacity
+constexpr int kRankMax = 256;   // descend until the boundary bin is at most this large
+constexpr int kMaxNW = 1024 / kWave;
 
 struct SelectShared {
-  uint32_t hist[kCopies * kCopyStride];
-  uint32_t bins[256];
-  int wsum[kSelectThreads / kWave];
-  int scan[4];
-  uint32_t sel_digit;
-  int sel_before;
-  int total;
+  uint32_t hist[kBins];
+  uint32_t lkey[kListCap];
+  int lidx[kListCap];
+  int wred[3][kMaxNW];
+  int wscan[kMaxNW];
+  int list_n;
+  uint32_t sel_bin;
+  int sel_above;
+  // fallback radix state
+  uint32_t bins256[256];
 };
-
-// Inclusive prefix over threads 0..255 of v (other threads get 0).  All
-// threads of the block must call it.
-__device__ __forceinline__ int scan256(int v, SelectShared& sh) {
-  const int w = threadIdx.x / kWave;
-  int x = 0;
-  if (threadIdx.x < 256) {
-    x = wave_incl_scan(v);
-    if (lane_id() == kWave - 1) sh.scan[w] = x;
-  }
-  __syncthreads();
-  if (threadIdx.x < 256)
-    for (int i = 0; i < w; ++i) x += sh.scan[i];
-  __syncthreads();
-  return x;
-}
-
-__device__ __forceinline__ void clear_hist(SelectShared& sh) {
-  for (int i = threadIdx.x; i < kCopies * kCopyStride; i += kSelectThreads) sh.hist[i] = 0;
-}
-
-// Sum the histogram copies into bins[]; then pick the digit that holds rank
-// `rank` (1-based), counting from the largest digit when `descending`, from
-// the smallest otherwise.  Returns the digit; *before = entries ranked
-// ahead of that digit.
-__device__ uint32_t pick_digit(SelectShared& sh, int rank, bool descending, int* before) {
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int c = 0; c < kCopies; ++c) s += sh.hist[c * kCopyStride + threadIdx.x];
-    sh.bins[threadIdx.x] = s;
-  }
-  __syncthreads();
-  const int d = descending ? 255 - (int)threadIdx.x : (int)threadIdx.x;
-  const int cnt = (threadIdx.x < 256) ? (int)sh.bins[d] : 0;
-  const int incl = scan256(cnt, sh);
-  if (threadIdx.x < 256) {
-    const int excl = incl - cnt;
-    if (excl < rank && rank <= incl) {
-      sh.sel_digit = (uint32_t)d;
-      sh.sel_before = excl;
-    }
-  }
-  __syncthreads();
-  *before = sh.sel_before;
-  return sh.sel_digit;
-}
 
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
   if (a.mode == kModeGather) return a.n_cols;
@@ -89,10 +55,44 @@ __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
   return min(lim + 1, a.n_cols);
 }
 
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a, int cache_cap) {
-  __shared__ SelectShared sh;
-  extern __shared__ uint32_t skeys[];
+// Inverse of order_key (for eligible keys).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
+__device__ __forceinline__ uint32_t load_key(const float* row, int c) {
+  const float v = row[c];
+  return v == neg_inf() ? kKeyExcluded : order_key(v);
+}
+
+// Block-wide exclusive scan of one int per thread; also returns the total.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* total, SelectShared& sh) {
+  constexpr int kNW = NT / kWave;
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) sh.wscan[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) {
+    const int s = sh.wscan[i];
+    before += (i < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+// NT threads per row.  KPT > 0: each thread keeps the keys of columns
+// tid + i*NT (i < KPT) in registers.  KPT == 0: rows of any length, re-read
+// from global memory in batches of 8 loads per thread.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
+  constexpr int kSelectThreads = NT;
+  constexpr int kNW = NT / kWave;
+  __shared__ SelectShared sh;
   const long long frow = a.row0 + blockIdx.x;
   const int b = (int)(frow / a.n_rows), r = (int)(frow % a.n_rows);
   const float* row = a.scores + (long long)blockIdx.x * a.ld;
@@ -103,124 +103,328 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a, in
     crow = a.cand + ((long long)b * n_g + r / a.group) * a.n_cols;
   }
   const int len = row_length(a, r);
-  const bool cached = len <= cache_cap;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  const int copy = lane & (kCopies - 1);
+  constexpr int REG = KPT > 0 ? KPT : 1;
+  uint32_t keys[REG];
 
-  auto key_at = [&](int c) -> uint32_t {
-    if (cached) return skeys[c];
-    const float v = row[c];
-    return v == neg_inf() ? kKeyExcluded : order_key(v);
+  auto idx_at = [&](int c) -> int { return crow ? crow[c] : c; };
+  auto key_at = [&](int c) -> uint32_t { return load_key(row, c); };
+  // Calls f(column, key) for every column of this thread (eligible or not).
+  auto for_keys = [&](auto&& f) {
+    if (KPT > 0) {
+#pragma unroll
+      for (int i = 0; i < REG; ++i) f(i * kSelectThreads + tid, keys[i]);
+    } else {
+      for (int c0 = 0; c0 < len; c0 += 8 * kSelectThreads) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = row[min(c0 + j * kSelectThreads + tid, len - 1)];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + j * kSelectThreads + tid;
+          f(c, (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded);
+        }
+      }
+    }
   };
-  auto index_at = [&](int c) -> int { return crow ? crow[c] : c; };
 
-  // ---- load (and cache) the keys, count the eligible ones ----
+  // ---- 1. load (batched, clamped addresses), count, min, max ----
   int nv = 0;
-  for (int c = tid; c < len; c += kSelectThreads) {
-    const float v = row[c];
-    const uint32_t k = v == neg_inf() ? kKeyExcluded : order_key(v);
-    if (cached) skeys[c] = k;
-    nv += (k != kKeyExcluded);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (KPT > 0) {
+    // every load of the row at once (clamped addresses: no per-element branch)
+    float v[REG];
+#pragma unroll
+    for (int i = 0; i < REG; ++i) v[i] = row[min(i * kSelectThreads + tid, len - 1)];
+#pragma unroll
+    for (int i = 0; i < REG; ++i) {
+      const int c = i * kSelectThreads + tid;
+      keys[i] = (c < len && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
+    }
   }
+  for_keys([&](int, uint32_t k) {
+    if (k != kKeyExcluded) {
+      ++nv;
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  });
   nv = wave_sum(nv);
-  if (lane == 0) sh.wsum[wave] = nv;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+  }
+  if (lane == 0) {
+    sh.wred[0][wave] = nv;
+    sh.wred[1][wave] = (int)kmin;
+    sh.wred[2][wave] = (int)kmax;
+  }
   __syncthreads();
   int n_valid = 0;
-  for (int i = 0; i < kSelectThreads / kWave; ++i) n_valid += sh.wsum[i];
-  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < kNW; ++i) {
+    n_valid += sh.wred[0][i];
+    kmin = min(kmin, (uint32_t)sh.wred[1][i]);
+    kmax = max(kmax, (uint32_t)sh.wred[2][i]);
+  }
+  const int topk = a.topk;
+  const int kk = min(topk, n_valid);
 
-  // ---- threshold: winners are key > tau, or key == tau with index <= idx_thr ----
-  uint32_t tau = kKeyExcluded;
-  int idx_thr = -1;
-  if (n_valid > a.topk) {
-    uint32_t prefix = 0, pmask = 0;
-    int rank = a.topk, before = 0, eq_count = 0;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      clear_hist(sh);
-      __syncthreads();
-      for (int c = tid; c < len; c += kSelectThreads) {
-        const uint32_t k = key_at(c);
-        if (k != kKeyExcluded && (k & pmask) == prefix)
-          atomicAdd(&sh.hist[copy * kCopyStride + ((k >> shift) & 255u)], 1u);
-      }
-      const uint32_t d = pick_digit(sh, rank, true, &before);
-      eq_count = (int)sh.bins[d];
-      rank -= before;
-      prefix |= d << shift;
-      pmask |= 255u << shift;
-      __syncthreads();
+  // ---- 2. narrow the boundary interval [blo, bhi] of keys ----
+  // `above` eligible keys lie above the interval and `need` of the keys inside
+  // it still win.  Winners = keys above the interval, plus either all of it
+  // or its `need` best entries in (key desc, index asc) order.
+  uint32_t blo = kmin, bhi = kmax;
+  int above = 0, need = kk, in_bin = n_valid;
+  bool idx_radix = false;
+  int idx_thr = 0;
+
+  // Suffix scan over the histogram: picks the bin holding rank `need`
+  // (descending); returns the bin, and the count above it via *before.
+  auto pick_desc = [&](int* before_out) -> uint32_t {
+    constexpr int BPT = kBins / NT;
+    int cnt[BPT], s = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      cnt[j] = (int)sh.hist[kBins - 1 - (BPT * tid + j)];
+      s += cnt[j];
     }
-    tau = prefix;
-    if (rank == eq_count) {
-      idx_thr = 0x7FFFFFFF;
-    } else {
-      // the rank-th smallest key index among the entries equal to tau
-      uint32_t ip = 0, im = 0;
-      for (int pass = 0; pass < 4; ++pass) {
-        const int shift = 24 - 8 * pass;
-        clear_hist(sh);
-        __syncthreads();
-        for (int c = tid; c < len; c += kSelectThreads) {
-          if (key_at(c) == tau) {
-            const uint32_t ix = (uint32_t)index_at(c);
-            if ((ix & im) == ip) atomicAdd(&sh.hist[copy * kCopyStride + ((ix >> shift) & 255u)], 1u);
-          }
+    int total;
+    int before = block_excl_scan<NT>(s, &total, sh);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      if (before < need && need <= before + cnt[j]) {
+        sh.sel_bin = (uint32_t)(kBins - 1 - (BPT * tid + j));
+        sh.sel_above = before;
+      }
+      before += cnt[j];
+    }
+    __syncthreads();
+    *before_out = sh.sel_above;
+    return sh.sel_bin;
+  };
+
+  if (n_valid > topk) {
+    // 2a. one pass of 2048 bins linear in the score value between the row's
+    // minimum and maximum (a monotone map: a larger score never lands in a
+    // lower bin), which spreads the bulk of a row over many bins
+    const float vlo = key_to_float(blo), vhi = key_to_float(bhi);
+    const float scale = (float)(kBins - 1) / (vhi - vlo);
+    if (vhi > vlo && scale > 0.f && scale < __builtin_huge_valf()) {
+      const float off = -vlo * scale;
+      auto lbin = [&](uint32_t k) {
+        const float x = __builtin_fmaf(key_to_float(k), scale, off);
+        return (uint32_t)min(max((int)x, 0), kBins - 1);
+      };
+      for (int i = tid; i < kBins; i += kSelectThreads) sh.hist[i] = 0;
+      __syncthreads();
+      for_keys([&](int, uint32_t k) {
+        if (k != kKeyExcluded) atomicAdd(&sh.hist[lbin(k)], 1u);
+      });
+      __syncthreads();
+      int before;
+      const uint32_t b = pick_desc(&before);
+      above += before;
+      need -= before;
+      in_bin = (int)sh.hist[b];
+      // the key range of that bin
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+      for_keys([&](int, uint32_t k) {
+        if (k != kKeyExcluded && lbin(k) == b) {
+          mn = min(mn, k);
+          mx = max(mx, k);
         }
-        const uint32_t d = pick_digit(sh, rank, false, &before);
-        rank -= before;
-        ip |= d << shift;
-        im |= 255u << shift;
+      });
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+      }
+      if (lane == 0) {
+        sh.wred[1][wave] = (int)mn;
+        sh.wred[2][wave] = (int)mx;
+      }
+      __syncthreads();
+      blo = 0xFFFFFFFFu;
+      bhi = 0u;
+#pragma unroll
+      for (int i = 0; i < kNW; ++i) {
+        blo = min(blo, (uint32_t)sh.wred[1][i]);
+        bhi = max(bhi, (uint32_t)sh.wred[2][i]);
+      }
+      __syncthreads();
+    }
+    // 2b. MSB-first radix descent in 11-bit digits inside [blo, bhi]
+    while (in_bin > kRankMax && blo != bhi && in_bin != need) {
+      const uint32_t diff = blo ^ bhi;
+      const int S = 32 - __builtin_clz(diff);  // bits >= S are shared by the interval
+      const int w = S < 11 ? S : 11;
+      const int shift = S - w;
+      const uint32_t dmask = (1u << w) - 1u;
+      for (int i = tid; i < kBins; i += kSelectThreads) sh.hist[i] = 0;
+      __syncthreads();
+      const uint32_t lo = blo, hi = bhi;
+      for_keys([&](int, uint32_t k) {
+        if (k != kKeyExcluded && k >= lo && k <= hi) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
+      });
+      __syncthreads();
+      int before;
+      const uint32_t d = pick_desc(&before);
+      above += before;
+      need -= before;
+      in_bin = (int)sh.hist[d];
+      const uint32_t base = S >= 32 ? 0u : (lo >> S) << S;
+      const uint32_t dlo = base | (d << shift);
+      const uint32_t dhi = dlo + ((1u << shift) - 1u);
+      blo = max(blo, dlo);
+      bhi = min(bhi, dhi);
+      __syncthreads();
+    }
+    if (in_bin != need) {
+      if (in_bin <= kListCap) {
+        // ---- 3. gather the boundary interval and rank it exactly ----
+        if (tid == 0) sh.list_n = 0;
         __syncthreads();
+        const uint32_t lo = blo, hi = bhi;
+        for_keys([&](int c, uint32_t k) {
+          if (k != kKeyExcluded && k >= lo && k <= hi) {
+            const int slot = atomicAdd(&sh.list_n, 1);
+            sh.lkey[slot] = k;
+            sh.lidx[slot] = idx_at(c);
+          }
+        });
+        __syncthreads();
+        const int m = sh.list_n;
+        for (int i = tid; i < m; i += kSelectThreads) {
+          const uint32_t ki = sh.lkey[i];
+          const int xi = sh.lidx[i];
+          int rank = 0;
+          for (int j = 0; j < m; ++j) {
+            const uint32_t kj = sh.lkey[j];
+            rank += (kj > ki) || (kj == ki && sh.lidx[j] < xi);
+          }
+          if (rank < need) out[above + rank] = xi;
+        }
+      } else {
+        // blo == bhi: a class of more than kListCap equal keys; `need` of them
+        // win by smallest key index (ascending radix over the indices)
+        idx_radix = true;
+        const uint32_t tau = blo;
+        uint32_t ip = 0, im = 0;
+        int rank = need;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          for (int i = tid; i < 256; i += kSelectThreads) sh.bins256[i] = 0;
+          __syncthreads();
+          for_keys([&](int c, uint32_t k) {
+            if (k == tau) {
+              const uint32_t ix = (uint32_t)idx_at(c);
+              if ((ix & im) == ip) atomicAdd(&sh.bins256[(ix >> shift) & 255u], 1u);
+            }
+          });
+          __syncthreads();
+          if (tid == 0) {
+            int below = 0;
+            for (int d = 0; d < 256; ++d) {
+              const int n = (int)sh.bins256[d];
+              if (below + n >= rank) {
+                sh.sel_bin = (uint32_t)d;
+                sh.sel_above = below;
+                break;
+              }
+              below += n;
+            }
+          }
+          __syncthreads();
+          rank -= sh.sel_above;
+          ip |= sh.sel_bin << shift;
+          im |= 255u << shift;
+          __syncthreads();
+        }
+        idx_thr = (int)ip;
       }
-      idx_thr = (int)ip;
     }
   }
+  const bool whole = in_bin == need;
 
-  // ---- ordered compaction of the winners ----
-  int base = 0;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int c0 = 0; c0 < len; c0 += kSelectThreads) {
-    const int c = c0 + tid;
-    bool win = false;
-    int ix = 0;
-    if (c < len) {
-      const uint32_t k = key_at(c);
-      if (k != kKeyExcluded && k > tau) {
-        win = true;
-        ix = index_at(c);
-      } else if (k != kKeyExcluded && k == tau) {
-        ix = index_at(c);
-        win = ix <= idx_thr;
-      }
-    }
-    const unsigned long long m = __ballot(win);
-    if (lane == 0) sh.wsum[wave] = __popcll(m);
-    __syncthreads();
-    int off = base, total = 0;
-    for (int i = 0; i < kSelectThreads / kWave; ++i) {
-      if (i < wave) off += sh.wsum[i];
-      total += sh.wsum[i];
-    }
-    if (win) out[off + __popcll(m & lt)] = ix;
-    base += total;
-    __syncthreads();
+  // ---- 4. compaction: keys above the interval (and all of it when it all wins) ----
+  const uint32_t cut_hi = bhi, cut_lo = blo;
+  auto certain = [&](uint32_t k) -> bool {
+    return k != kKeyExcluded && (k > cut_hi || (whole && k >= cut_lo));
+  };
+  int mine = 0;
+  for_keys([&](int, uint32_t k) { mine += certain(k); });
+  int total;
+  int off = block_excl_scan<NT>(mine, &total, sh);
+  for_keys([&](int c, uint32_t k) {
+    if (certain(k)) out[off++] = idx_at(c);
+  });
+  if (idx_radix) {
+    const uint32_t tau = blo;
+    int tmine = 0;
+    for_keys([&](int c, uint32_t k) { tmine += (k == tau && idx_at(c) <= idx_thr); });
+    int ttot;
+    int toff = above + block_excl_scan<NT>(tmine, &ttot, sh);
+    for_keys([&](int c, uint32_t k) {
+      if (k == tau && idx_at(c) <= idx_thr) out[toff++] = idx_at(c);
+    });
   }
-  for (int i = base + tid; i < a.topk; i += kSelectThreads) out[i] = -1;
+  for (int i = kk + tid; i < topk; i += kSelectThreads) out[i] = -1;
 }
 
-hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)select_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 16 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const int cap = a.n_cols < kSelectCache ? a.n_cols : kSelectCache;
-  hipLaunchKernelGGL(select_kernel, dim3(n_launch_rows), dim3(kSelectThreads),
-                     (size_t)cap * sizeof(uint32_t), st, a, cap);
+template <int NT, int KPT>
+static hipError_t launch_kpt(const SelectArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL((select_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, st, a);
   return hipGetLastError();
+}
+
+static hipError_t launch_by_length(const SelectArgs& a, int rows, int n, hipStream_t st) {
+  if (n <= 256 * 8) return launch_kpt<256, 8>(a, rows, st);
+  if (n <= 512 * 16) return launch_kpt<512, 16>(a, rows, st);
+  if (n <= 1024 * 16) return launch_kpt<1024, 16>(a, rows, st);
+  if (n <= 1024 * 32) return launch_kpt<1024, 32>(a, rows, st);
+  return launch_kpt<1024, 0>(a, rows, st);
+}
+
+// Rows of a dense or proxy launch grow in length with the row index within a
+// sequence; such launches are split into length classes so that each class
+// runs the smallest variant that holds its rows.
+hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st) {
+  if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
+  const int classes[4] = {256 * 8, 512 * 16, 1024 * 16, 1024 * 32};
+  long long r = 0;
+  while (r < n_launch_rows) {
+    // the length of launch row r, and the longest run of rows in its class
+    auto len_of = [&](long long i) {
+      const long long fr = a.row0 + i;
+      const int rr = (int)(fr % a.n_rows);
+      const int lim = (a.mode == kModeProxy) ? a.q_pos0 + std::min((rr + 1) * a.group, a.n_q) - 1
+                                             : a.q_pos0 + rr;
+      return std::min(lim + 1, a.n_cols);
+    };
+    int cls = 4;
+    for (int c = 0; c < 4; ++c)
+      if (len_of(r) <= classes[c]) { cls = c; break; }
+    long long e = r + 1;
+    while (e < n_launch_rows) {
+      const int l = len_of(e);
+      int ce = 4;
+      for (int c = 0; c < 4; ++c)
+        if (l <= classes[c]) { ce = c; break; }
+      if (ce != cls) break;
+      ++e;
+    }
+    SelectArgs sub = a;
+    sub.scores = a.scores + r * a.ld;
+    sub.row0 = a.row0 + r;
+    const int n = cls < 4 ? classes[cls] : a.n_cols;
+    hipError_t err = launch_by_length(sub, (int)(e - r), n < a.n_cols ? n : a.n_cols, st);
+    if (err != hipSuccess) return err;
+    r = e;
+  }
+  return hipSuccess;
 }
 
 __global__ void fill_kernel(float* p, size_t n, float v) {

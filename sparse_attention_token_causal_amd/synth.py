@@ -15,6 +15,12 @@ top-k tokens and scores are long-tailed along the key axis):
   chosen rows scaled by 4 (heavy-tailed keys);
 * head weights: U(0,1).
 
+Two further structures exist only to exercise the select's tie handling:
+small-integer queries, keys and weights ("int": values in {-2..2}, weights
+in {0, 1, 2}), where many scores are exactly equal, and identical keys
+("const": every key row is the same N(0,1) vector), where every score of a
+query ties.
+
 Draw order per call: query noise, keys, heavy-row choice, weights, all from
 one torch generator seeded with ``seed`` on the target device.
 """
@@ -37,13 +43,14 @@ class Workload:
     dim: int
     q_fmt: str          # "f32" | "bf16" | "fp8"
     k_fmt: str
-    q_dist: str         # "normal8" | "ar1"
-    k_dist: str         # "normal8" | "heavy"
+    q_dist: str         # "normal8" | "ar1" | "int"
+    k_dist: str         # "normal8" | "heavy" | "int" | "const"
     rho: float = 0.0
     topk: int = 2048
     group: int = 0      # 0: dense only
     n_cand: int = 0
     seed: int = 0
+    w_dist: str = "uniform"  # "uniform" | "int"
 
     @property
     def q_pos0(self):
@@ -113,12 +120,18 @@ def make_inputs(wl: Workload, device="cpu"):
         q = eps / 8.0
     elif wl.q_dist == "ar1":
         q = _ar1(eps, wl.rho)
+    elif wl.q_dist == "int":
+        q = torch.clamp(torch.round(eps * 1.5), -2, 2)
     else:
         raise ValueError(wl.q_dist)
     del eps
     k = torch.randn((B, nk, d), generator=g, device=device, dtype=torch.float32)
     if wl.k_dist == "normal8":
         k = k / 8.0
+    elif wl.k_dist == "int":
+        k = torch.clamp(torch.round(k * 1.5), -2, 2)
+    elif wl.k_dist == "const":
+        k = k[:, :1].expand(B, nk, d).clone()
     elif wl.k_dist == "heavy":
         n_heavy = nk // 100
         for b in range(B):
@@ -127,6 +140,8 @@ def make_inputs(wl: Workload, device="cpu"):
     else:
         raise ValueError(wl.k_dist)
     w = torch.rand((B, nq, H), generator=g, device=device, dtype=torch.float32)
+    if wl.w_dist == "int":
+        w = torch.floor(w * 3.0)
     qs, q_scale = _store(q, wl.q_fmt, (2, 3))
     del q
     ks, k_scale = _store(k, wl.k_fmt, (2,))

@@ -30,6 +30,14 @@ DENSE = [
     Workload("f32_nq150_nk300_H64_d64", 1, 150, 300, 64, 64, "f32", "f32", "normal8", "heavy", topk=16, seed=6),
     Workload("bf16_L1_k4", 1, 1, 1, 64, 128, "bf16", "bf16", "normal8", "normal8", topk=4, seed=7),
     Workload("bf16_L90_k1", 1, 90, 90, 32, 128, "bf16", "bf16", "normal8", "heavy", topk=1, seed=8),
+    # tie-heavy rows: every score of a query equal (boundary bin beyond the LDS list
+    # for prefixes above 2048 -> radix fallback), and small integers (many exact ties)
+    Workload("ties_const_keys_L3000_k1000", 1, 3000, 3000, 32, 64, "bf16", "bf16", "normal8", "const",
+             topk=1000, seed=9),
+    Workload("ties_int_L2500_k300", 1, 2500, 2500, 16, 64, "bf16", "bf16", "int", "int", topk=300, seed=10,
+             w_dist="int"),
+    Workload("ties_int_f32_decode_B2_k700", 2, 3, 9000, 16, 64, "f32", "f32", "int", "int", topk=700,
+             seed=11, w_dist="int"),
 ]
 
 
@@ -96,6 +104,8 @@ GROUPED = [
              topk=256, group=2, n_cand=512, seed=14),
     Workload("g_bf16_L30_G100", 1, 30, 30, 32, 64, "bf16", "bf16", "normal8", "heavy", topk=8, group=100,
              n_cand=12, seed=15),
+    Workload("g_ties_int_L600_G8_C300", 1, 600, 600, 16, 64, "bf16", "bf16", "int", "int", topk=100, group=8,
+             n_cand=300, seed=16, w_dist="int"),
 ]
 
 
