@@ -97,30 +97,38 @@ __device__ __forceinline__ int row_limit(const ScoreArgs& a, int r) {
   return a.q_pos0 + r;
 }
 
-template <int QF, int KF, int H, int D>
+// Scheduling groups for the instruction scheduler (gfx9 sched_group_barrier masks).
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+// GATHER: columns are the group's candidate list (PIVOT-Refine); otherwise the
+// columns are key positions (dense scan, proxy scan).
+template <int QF, int KF, int H, int D, int RW, bool GATHER>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   typedef MfmaTraits<QF, KF> M;
   constexpr int NKS = D / M::KSTEP;
   constexpr int ROWB = D * M::KE + 16;
   constexpr int QW = 64 / H;                  // queries per wave
   constexpr int NW = kScoreThreads / kWave;   // 8 waves
+  constexpr int KW = NW / RW, TW = KW * 64;   // key-waves, tile width (columns)
   constexpr bool WIDEN = (KF == FP8 && QF == BF16);
   constexpr int CPC = D * M::GE / 16;         // 16-byte global chunks per key row
+  constexpr int NCH = (TW * CPC + kScoreThreads - 1) / kScoreThreads;  // chunks per thread per tile
+  constexpr int TILE_BYTES = TW * ROWB + TW * 8;
+  // per-column data (key index, key scale) is only needed for gathered
+  // columns or FP8 keys; dense scans of BF16/F32 keys use the position itself
+  constexpr bool COLINFO = GATHER || KF == FP8;
 
+  // two tile buffers: [TW][ROWB] key rows, then TW column keys and TW scales
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int RW = a.rw, KW = NW / RW, TW = KW * 64;
-  char* ktile = smem;
-  int* colkey = (int*)(smem + TW * ROWB);
-  float* colscale = (float*)(colkey + TW);
 
   const int wave = threadIdx.x / kWave, l = lane_id(), half = l >> 5, l32 = l & 31;
   const int rw = wave % RW, kw = wave / RW;
-  const int BQ = RW * QW;
+  constexpr int BQ = RW * QW;
 
   // ---- which rows this workgroup owns (longest prefixes first) ----
   const int bid = a.blk0 + (a.n_blocks - 1 - (int)blockIdx.x);
   int b, r_begin, r_end, g = 0;
-  if (a.mode != kModeGather) {
+  if (!GATHER) {
     const int bps = (a.n_rows + BQ - 1) / BQ;
     b = bid / bps;
     r_begin = (bid % bps) * BQ;
@@ -135,9 +143,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     r_end = min(r_begin + BQ, ge);
     if (r_begin >= r_end) return;
   }
-  int c_begin = (int)blockIdx.y * a.kc;
+  const int c_begin = (int)blockIdx.y * a.kc;
   int c_end = min(c_begin + a.kc, a.n_cols);
-  if (a.mode != kModeGather) c_end = min(c_end, row_limit(a, r_end - 1) + 1);
+  if (!GATHER) c_end = min(c_end, row_limit(a, r_end - 1) + 1);
   if (c_begin >= c_end) return;
 
   // ---- resident q fragments and head weights of this wave's 64 rows ----
@@ -170,99 +178,203 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     }
   }
 
-  const int n_g_all = (a.mode == kModeGather) ? (a.n_q + a.group - 1) / a.group : 0;
-  const int* cand_row = (a.mode == kModeGather) ? a.cand + ((size_t)b * n_g_all + g) * a.n_cols : nullptr;
+  const int* cand_row = nullptr;
+  if (GATHER) cand_row = a.cand + ((size_t)b * ((a.n_q + a.group - 1) / a.group) + g) * a.n_cols;
   const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * M::GE;
 
-  for (int c0 = c_begin; c0 < c_end; c0 += TW) {
-    // ---- stage the key tile (TW columns) in LDS ----
-    for (int i = threadIdx.x; i < TW * CPC; i += kScoreThreads) {
+  // ---- staging of one key tile: global -> registers -> LDS (double buffered) ----
+  // Loads are unconditional: a column past the range or an empty candidate
+  // slot reads a valid key row (it is masked in the epilogue), so the loads
+  // of a tile are all in flight together while the current tile computes.
+  i32x4 stage[NCH];
+  int stage_key[NCH];
+  auto stage_load = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int i = min((int)threadIdx.x + u * kScoreThreads, TW * CPC - 1);
       const int j = i / CPC, c = i % CPC;
-      const int col = c0 + j;
-      int s = -1;
-      if (col < c_end) s = (a.mode == kModeGather) ? cand_row[col] : col;
-      const bool ok = (s >= 0 && s < a.n_k);
-      i32x4 v = {0, 0, 0, 0};
-      if (ok) v = *(const i32x4*)(kseq + ((size_t)s * D * M::GE) + c * 16);
-      if (WIDEN) {
-        uint32_t o[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4((uint32_t)v[e], o[2 * e], o[2 * e + 1]);
-        i32x4* dst = (i32x4*)(ktile + j * ROWB + c * 32);
-        dst[0] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
-        dst[1] = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      const int col = min(c0 + j, c_end - 1);
+      int s, srow;
+      if (GATHER) {
+        s = cand_row[col];
+        if (c0 + j >= c_end || s >= a.n_k) s = -1;
+        srow = s < 0 ? 0 : s;
       } else {
-        *(i32x4*)(ktile + j * ROWB + c * 16) = v;
+        s = c0 + j < c_end ? col : -1;
+        srow = col;
       }
-      if (c == 0) {
-        colkey[j] = ok ? s : -1;
-        colscale[j] = (ok && KF == FP8) ? a.k_scale[(size_t)b * a.n_k + s] : 1.f;
+      stage_key[u] = s;
+      stage[u] = *(const i32x4*)(kseq + ((size_t)srow * D * M::GE) + c * 16);
+    }
+  };
+  auto stage_store = [&](int buf) {
+    char* kt = smem + buf * TILE_BYTES;
+    int* ck = (int*)(kt + TW * ROWB);
+    float* cs = (float*)(ck + TW);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int i = threadIdx.x + u * kScoreThreads;
+      if (NCH * kScoreThreads == TW * CPC || i < TW * CPC) {
+        const int j = i / CPC, c = i % CPC;
+        const i32x4 v = stage[u];
+        if (WIDEN) {
+          uint32_t o[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4((uint32_t)v[e], o[2 * e], o[2 * e + 1]);
+          i32x4* dst = (i32x4*)(kt + j * ROWB + c * 32);
+          dst[0] = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+          dst[1] = i32x4{(int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+        } else {
+          *(i32x4*)(kt + j * ROWB + c * 16) = v;
+        }
+        if (COLINFO && c == 0) {
+          const int s = stage_key[u];
+          ck[j] = s;
+          cs[j] = (s >= 0 && KF == FP8) ? a.k_scale[(size_t)b * a.n_k + s] : 1.f;
+        }
       }
     }
-    __syncthreads();
+  };
 
-    // ---- MFMA: 2 row blocks x 2 column blocks over d ----
-    f32x16 acc[2][2];
+  // ---- MFMA of one 32-column block over d, from LDS buffer `buf` ----
+  f32x16 acc[2][2];
+  // With few inner steps (bf16, fp8) every fragment of the block is read from
+  // LDS up front so the reads overlap; float32 (64 steps) reads step by step.
+  constexpr bool PRELOAD = NKS <= 8;
+  auto mfma_block = [&](int buf, int cb) {
+    const char* ldsrow = smem + buf * TILE_BYTES + (kw * 64 + cb * 32 + l32) * ROWB;
+    if constexpr (PRELOAD) {
+      typename M::frag bf[NKS];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+      for (int ks = 0; ks < NKS; ++ks) bf[ks] = M::load_b(ldsrow, ks, half);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        const char* ldsrow = ktile + (kw * 64 + cb * 32 + l32) * ROWB;
-        typename M::frag bf = M::load_b(ldsrow, ks, half);
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) acc[rb][cb] = M::mma(afrag[rb][ks], bf, acc[rb][cb]);
-      }
-    }
-
-    // ---- epilogue: ReLU, x w, sum over heads, scale, mask, store ----
-#pragma unroll
-    for (int qi = 0; qi < QW; ++qi) {
-      float tot[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        float p = 0.f;
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
+          acc[rb][cb] = M::mma(afrag[rb][ks], bf[ks], ks == 0 ? f32x16{} : acc[rb][cb]);
+    } else {
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if ((32 * rb + 8 * (v / 4)) / H == qi) p += wreg[rb][v] * fmaxf(acc[rb][cb][v], 0.f);
-        tot[cb] = p + xor32(p);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const typename M::frag bf = M::load_b(ldsrow, ks, half);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][cb] = M::mma(afrag[rb][ks], bf, ks == 0 ? f32x16{} : acc[rb][cb]);
       }
+    }
+  };
+  constexpr int NDSR = NKS * (int)(sizeof(typename M::frag) / 16);  // 16-byte LDS reads per block
+  // the block's fragment reads first, then one MFMA per few VALU ops
+#define IDX_INTERLEAVE(id)                                               \
+  if constexpr (PRELOAD) {                                               \
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NDSR, id);        \
+    _Pragma("unroll") for (int i_ = 0; i_ < 2 * NKS; ++i_) {             \
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, id);           \
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, id);           \
+    }                                                                    \
+  }
+
+  // ---- epilogue of one block: ReLU, x w, sum over heads, scale, mask, store ----
+  // The head sum is an in-lane weighted sum over the 16 result rows the lane
+  // holds, plus the other half-wave's partial (v_permlane32_swap).  Lanes
+  // 0-31 store column block 0 and lanes 32-63 block 1; `key`/`scale` describe
+  // this lane's column (kw*64 + half*32 + lane%32) of tile c0.
+  auto epilogue = [&](int cb, int c0, int key, float scale) {
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if ((32 * rb + 8 * (v / 4)) / H == qi) {
+            if (v & 1)
+              p1 = __builtin_fmaf(wreg[rb][v], fmaxf(acc[rb][cb][v], 0.f), p1);
+            else
+              p0 = __builtin_fmaf(wreg[rb][v], fmaxf(acc[rb][cb][v], 0.f), p0);
+          }
+      const float p = p0 + p1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      const float other = __uint_as_float(cb == 0 ? sw[1] : sw[0]);
+      const float tot = p + other;
       const int t = t_first + qi;
-      const int jl = kw * 64 + half * 32 + l32;  // lanes 0-31 store column block 0, 32-63 block 1
-      const int col = c0 + jl;
-      if (t < r_end && col < c_end) {
-        const int s = colkey[jl];
-        const bool ok = s >= 0 && s <= row_limit(a, t);
-        const float val = ok ? tot[half] * colscale[jl] : neg_inf();
+      const int col = c0 + kw * 64 + half * 32 + l32;
+      if (half == cb && t < r_end && col < c_end) {
+        const bool ok = key >= 0 && key <= row_limit(a, t);
+        const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
         a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
       }
     }
+  };
+
+  // ---- software-pipelined scan over the key tiles ----
+  // While the MFMAs of one column block run, the epilogue of the other block
+  // (of this tile or of the previous one) executes on the VALU; the next
+  // tile's global loads are in flight meanwhile, and one barrier per tile
+  // publishes the next LDS buffer.
+  stage_load(c_begin);
+  stage_store(0);
+  __syncthreads();
+  int buf = 0, prev_c0 = -1, key_prev = -1;
+  float scale_prev = 1.f;
+  const int jl = kw * 64 + half * 32 + l32;
+  for (int c0 = c_begin; c0 < c_end; c0 += TW) {
+    const bool has_next = c0 + TW < c_end;
+    if (has_next) stage_load(c0 + TW);
+    int key_cur = c0 + jl;
+    float scale_cur = 1.f;
+    if (COLINFO) {
+      const int* ck = (const int*)(smem + buf * TILE_BYTES + TW * ROWB);
+      key_cur = ck[jl];
+      scale_cur = ((const float*)(ck + TW))[jl];
+    }
+    mfma_block(buf, 0);
+    if (prev_c0 >= 0) epilogue(1, prev_c0, key_prev, scale_prev);
+    IDX_INTERLEAVE(0);
+    mfma_block(buf, 1);
+    epilogue(0, c0, key_cur, scale_cur);
+    IDX_INTERLEAVE(1);
+    if (has_next) stage_store(buf ^ 1);
     __syncthreads();
+    prev_c0 = c0;
+    key_prev = key_cur;
+    scale_prev = scale_cur;
+    buf ^= 1;
   }
+  if (prev_c0 >= 0) epilogue(1, prev_c0, key_prev, scale_prev);
+#undef IDX_INTERLEAVE
 }
 
-template <int QF, int KF, int H, int D>
-static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+template <int QF, int KF, int H, int D, int RW, bool GATHER>
+static hipError_t launch_mode(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D>,
+    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D, RW, GATHER>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((score_kernel<QF, KF, H, D>), grid, dim3(kScoreThreads), lds, st, a);
+  hipLaunchKernelGGL((score_kernel<QF, KF, H, D, RW, GATHER>), grid, dim3(kScoreThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int QF, int KF, int H, int D, int RW>
+static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (a.mode == kModeGather) return launch_mode<QF, KF, H, D, RW, true>(a, grid, lds, st);
+  return launch_mode<QF, KF, H, D, RW, false>(a, grid, lds, st);
+}
+
+template <int QF, int KF, int H, int D>
+static hipError_t pick_rw(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
+  if (a.rw == 2) return launch_one<QF, KF, H, D, 2>(a, grid, lds, st);
+  if (a.rw == 4) return launch_one<QF, KF, H, D, 4>(a, grid, lds, st);
+  if (a.rw == 8) return launch_one<QF, KF, H, D, 8>(a, grid, lds, st);
+  return hipErrorInvalidValue;
 }
 
 template <int QF, int KF, int H>
 static hipError_t pick_d(const ScoreArgs& a, int D, dim3 grid, size_t lds, hipStream_t st) {
-  if (D == 64) return launch_one<QF, KF, H, 64>(a, grid, lds, st);
-  if (D == 128) return launch_one<QF, KF, H, 128>(a, grid, lds, st);
+  if (D == 64) return pick_rw<QF, KF, H, 64>(a, grid, lds, st);
+  if (D == 128) return pick_rw<QF, KF, H, 128>(a, grid, lds, st);
   return hipErrorInvalidValue;
 }
 
@@ -278,7 +390,7 @@ size_t score_lds_bytes(int qf, int kf, int D, int rw) {
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
   const int tw = (kScoreThreads / kWave / rw) * 64;
   (void)kf;
-  return (size_t)tw * (D * ke + 16) + (size_t)tw * 8;
+  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8);  // double-buffered tiles
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
