@@ -81,9 +81,10 @@ def make_step(S, wl, inp, dev):
     dtype = "fp8" if wl.q_fmt == "fp8" else ("f32" if wl.q_fmt == "f32" else "bf16")
     if wl.group == 0 or wl.name.startswith("decode") or wl.name.startswith("prefill"):
         p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
-        # one workspace holding every score row: one score and one select launch per step
+        # a workspace for every row at once (score rows, or candidate lists of
+        # (score, key) slots and a count): one score and one select launch per step
         ws_bytes = max(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk),
-                       wl.batch * wl.n_q * wl.n_k * 4)
+                       wl.batch * wl.n_q * (wl.n_k * 8 + 4) + 4096)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         out = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device=dev)
 

@@ -138,9 +138,18 @@ long long buffer_rows(const Layout& L, long long total_rows) {
 
 // Score the rows block-chunk by block-chunk into `buf` and select each row's
 // top-k into `out`.  `full` = buf holds every row (row stride n_cols).
+// Candidate filtering (see ScoreArgs::filter) replaces full score rows by
+// per-row candidate lists in dense scans with one query per wave.
+struct Filter {
+  bool on = false;
+  float* val = nullptr;   // [rows, n_k]
+  int* idx = nullptr;     // [rows, n_k]
+  int* count = nullptr;   // [rows]
+};
+
 int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D, int B, int n_q,
                      int group, float* buf, long long buf_rows, bool full, int topk, int* out,
-                     hipStream_t st) {
+                     hipStream_t st, const Filter& flt = Filter()) {
   const int bpc = full ? L.total_blocks : (int)(buf_rows / L.BQ);
   if (bpc < 1) return IDX_EWORKSPACE;
   const int tw = (8 / L.rw) * 64;
@@ -150,7 +159,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     const long long r1 = block_start_row(L.mode, blk0 + nb, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
     if (r1 <= r0) continue;
     int chunks = 1;
-    if (nb < 1024) chunks = ceil_div(2048, nb);
+    if (nb < 1024 && !flt.on) chunks = ceil_div(2048, nb);  // filtering keeps whole rows
     int kc = ceil_div(L.n_cols, chunks);
     kc = ceil_div(kc, tw) * tw;
     chunks = ceil_div(L.n_cols, kc);
@@ -161,6 +170,13 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.ld = L.n_cols;
     sa.kc = kc;
     sa.rw = L.rw;
+    sa.nw = 8;
+    sa.filter = flt.on ? 1 : 0;
+    sa.cval = flt.val;
+    sa.cidx = flt.idx;
+    sa.ccount = flt.count;
+    sa.cld = L.n_cols;
+    sa.topk = topk;
     if (timed(IDX_KERNEL_SCORE, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
       return IDX_EHIP;
     SelectArgs se;
@@ -174,8 +190,16 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     se.n_q = n_q;
     se.group = group;
     se.cand = sa.cand;
+    se.lidx = nullptr;
+    se.counts = nullptr;
     se.topk = topk;
     se.out = out;
+    if (flt.on) {
+      se.mode = kModeList;
+      se.scores = flt.val;
+      se.lidx = flt.idx;
+      se.counts = flt.count;
+    }
     if (timed(IDX_KERNEL_SELECT, st, [&] { return launch_select(se, (int)(r1 - r0), st); }) != hipSuccess)
       return IDX_EHIP;
   }
@@ -198,6 +222,16 @@ ScoreArgs base_args(const idx_problem* p) {
   a.cand = nullptr;
   a.mode = kModeDense;
   return a;
+}
+
+// Dense scans with 64 heads run eight query-waves per workgroup, one query
+// per wave: those filter candidates instead of writing full score rows.
+bool use_filter(const idx_problem* p, const Layout& L) { return p->heads == 64 && L.rw == 8; }
+
+// Workspace bytes per buffered row of a dense scan: a float score row, or a
+// candidate list (float score + int key per slot) and its count.
+size_t score_row_bytes(const idx_problem* p, const Layout& L) {
+  return use_filter(p, L) ? (size_t)p->n_k * 8 + 4 : (size_t)p->n_k * 4;
 }
 
 int proxy_q_dtype(const idx_problem* p) { return p->q_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
@@ -230,7 +264,7 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
   if (check_problem(p) != IDX_OK) return 0;
   if (op == IDX_OP_SCORE_TOPK) {
     Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
-    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * p->n_k * 4);
+    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * score_row_bytes(p, L));
   }
   if (group < 1) return 0;
   const int n_g = ceil_div(p->n_q, group);
@@ -264,15 +298,25 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
           return launch_fill(out_scores, (size_t)rows * p->n_k, -__builtin_huge_valf(), st);
         }) != hipSuccess)
       return IDX_EHIP;
-  } else {
-    const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
-    if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
-    buf = (float*)ws;
-    rows = (long long)(ws_bytes / ((size_t)p->n_k * 4));
   }
   ScoreArgs sa = base_args(p);
+  if (full)
+    return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
+                            buf, rows, full, topk, out_idx, st);
+  const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
+  if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+  rows = (long long)(ws_bytes / score_row_bytes(p, L));
+  if (!use_filter(p, L))
+    return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
+                            (float*)ws, rows, false, topk, out_idx, st);
+  // layout: [rows, n_k] float scores, [rows, n_k] int keys, [rows] counts
+  Filter flt;
+  flt.on = true;
+  flt.val = (float*)ws;
+  flt.idx = (int*)((char*)ws + (size_t)rows * p->n_k * 4);
+  flt.count = (int*)((char*)ws + (size_t)rows * p->n_k * 8);
   return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
-                          buf, rows, full, topk, out_idx, st);
+                          nullptr, rows, false, topk, out_idx, st, flt);
 }
 
 int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand,

@@ -27,6 +27,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (for keys of finite values).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 __device__ __forceinline__ float neg_inf() { return __uint_as_float(0xFF800000u); }
 
 // bfloat16 bits of an exactly representable float (truncation is exact when

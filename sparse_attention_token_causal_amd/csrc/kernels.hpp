@@ -7,7 +7,6 @@
 
 namespace idx {
 
-constexpr int kScoreThreads = 512;   // 8 waves per score workgroup
 constexpr int kSelectThreads = 512;  // 8 waves per select workgroup
 constexpr int kSelectCache = 32768;  // row keys kept in LDS by the select (128 KiB)
 
@@ -15,6 +14,7 @@ constexpr int kSelectCache = 32768;  // row keys kept in LDS by the select (128 
 constexpr int kModeDense = 0;   // rows = queries, columns = key positions, row limit q_pos0 + t
 constexpr int kModeProxy = 1;   // rows = group proxies, row limit = last member's position
 constexpr int kModeGather = 2;  // rows = queries, columns = the group's candidate list
+constexpr int kModeList = 3;    // select only: rows are candidate lists (score, key index)
 
 struct ScoreArgs {
   const void* q;          // [B, n_rows, H, D] rows (queries or proxies)
@@ -31,7 +31,19 @@ struct ScoreArgs {
   float* out;             // scores, row stride ld
   long long ld;
   int kc;                 // key columns per workgroup (grid.y = ceil(n_cols / kc))
-  int rw;                 // row-waves per workgroup (1, 2, 4, 8); 64 (query, head) rows each
+  int rw;                 // row-waves per workgroup (2, 4, 8); 64 (query, head) rows each
+  int nw;                 // waves per workgroup: 8, or 4 (with rw = 4)
+  // Candidate filtering (dense scans with one query per wave, whole rows per
+  // workgroup): instead of full score rows, each row's candidates - every key
+  // whose score reaches the row's running threshold bin - are written as
+  // (score, key) pairs at cval/cidx + (row - row0) * cld and their number at
+  // ccount[row - row0].  `topk` sets the threshold.
+  int filter;
+  float* cval;
+  int* cidx;
+  int* ccount;
+  long long cld;
+  int topk;
 };
 
 struct SelectArgs {
@@ -40,14 +52,17 @@ struct SelectArgs {
   long long row0;
   int n_rows;             // rows per sequence (queries or proxies)
   int n_cols;
-  int mode;               // kModeDense / kModeProxy: length = limit + 1; kModeGather: all n_cols, -inf = excluded
+  int mode;               // kModeDense / kModeProxy: length = limit + 1; kModeGather: all n_cols, -inf = excluded;
+                          // kModeList: length = counts[i], key index = lidx[i * ld + c]
   int q_pos0, n_q, group;
   const int* cand;        // gather: key index of each column
+  const int* lidx;        // list: key indices, same layout as scores
+  const int* counts;      // list: entries per launch row
   int topk;
   int* out;               // [B * n_rows, topk], indexed by flattened row
 };
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw);
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter);
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st);

@@ -26,6 +26,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace idx {
 
 template <int QF, int KF>
@@ -102,13 +104,18 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
 // GATHER: columns are the group's candidate list (PIVOT-Refine); otherwise the
 // columns are key positions (dense scan, proxy scan).
-template <int QF, int KF, int H, int D, int RW, bool GATHER>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
+// Filtering: bins of the running per-row histogram (256 per octave of the
+// score, a window of 8 octaves placed from the first tile's largest score).
+constexpr int kFiltBins = 2048;
+
+template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER>
+__global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
+  constexpr int kScoreThreads = NWV * 64;  // threads of this workgroup
   typedef MfmaTraits<QF, KF> M;
   constexpr int NKS = D / M::KSTEP;
   constexpr int ROWB = D * M::KE + 16;
   constexpr int QW = 64 / H;                  // queries per wave
-  constexpr int NW = kScoreThreads / kWave;   // 8 waves
+  constexpr int NW = NWV;                     // waves per workgroup
   constexpr int KW = NW / RW, TW = KW * 64;   // key-waves, tile width (columns)
   constexpr bool WIDEN = (KF == FP8 && QF == BF16);
   constexpr int CPC = D * M::GE / 16;         // 16-byte global chunks per key row
@@ -117,6 +124,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // per-column data (key index, key scale) is only needed for gathered
   // columns or FP8 keys; dense scans of BF16/F32 keys use the position itself
   constexpr bool COLINFO = GATHER || KF == FP8;
+  static_assert(!FILTER || (!GATHER && QW == 1), "filtering: dense scans, one query per wave");
 
   // two tile buffers: [TW][ROWB] key rows, then TW column keys and TW scales
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -178,6 +186,20 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
     }
   }
 
+  // ---- filtering state (one query per wave; wave-uniform) ----
+  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES) + wave * kFiltBins;
+  int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0;
+  float f_lo = neg_inf();  // lower edge of bin f_theta (-inf while f_theta == 0)
+  bool f_based = false;
+  float* f_val = nullptr;
+  int* f_idx = nullptr;
+  if constexpr (FILTER) {
+    for (int i = l; i < kFiltBins; i += kWave) hist[i] = 0;
+    const long long crow = (long long)b * a.n_rows + t_first - a.row0;
+    f_val = a.cval + crow * a.cld;
+    f_idx = a.cidx + crow * a.cld;
+  }
+
   const int* cand_row = nullptr;
   if (GATHER) cand_row = a.cand + ((size_t)b * ((a.n_q + a.group - 1) / a.group) + g) * a.n_cols;
   const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * M::GE;
@@ -186,9 +208,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // Loads are unconditional: a column past the range or an empty candidate
   // slot reads a valid key row (it is masked in the epilogue), so the loads
   // of a tile are all in flight together while the current tile computes.
-  i32x4 stage[NCH];
-  int stage_key[NCH];
-  auto stage_load = [&](int c0) {
+  i32x4 stage_buf[2][NCH];
+  int stage_keys[2][NCH];
+  auto stage_load = [&](auto set_c, int c0) {
+    constexpr int SET = decltype(set_c)::value;
+    i32x4* stage = stage_buf[SET];
+    int* stage_key = stage_keys[SET];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int i = min((int)threadIdx.x + u * kScoreThreads, TW * CPC - 1);
@@ -207,7 +232,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       stage[u] = *(const i32x4*)(kseq + ((size_t)srow * D * M::GE) + c * 16);
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](auto set_c, int buf) {
+    constexpr int SET = decltype(set_c)::value;
+    const i32x4* stage = stage_buf[SET];
+    const int* stage_key = stage_keys[SET];
     char* kt = smem + buf * TILE_BYTES;
     int* ck = (int*)(kt + TW * ROWB);
     float* cs = (float*)(ck + TW);
@@ -238,47 +266,53 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
 
   // ---- MFMA of one 32-column block over d, from LDS buffer `buf` ----
   f32x16 acc[2][2];
-  // With few inner steps (bf16, fp8) every fragment of the block is read from
-  // LDS up front so the reads overlap; float32 (64 steps) reads step by step.
+  // With few inner steps (bf16, fp8) the fragments of a block are read from
+  // LDS ahead of its MFMAs: block 0's at the top of the tile, block 1's while
+  // block 0 computes.  Float32 (64 steps) reads step by step.
   constexpr bool PRELOAD = NKS <= 8;
-  auto mfma_block = [&](int buf, int cb) {
+  typedef typename M::frag frag_t;
+  frag_t bfA[PRELOAD ? NKS : 1], bfB[PRELOAD ? NKS : 1];
+  auto load_block = [&](frag_t* bf, int buf, int cb) {
     const char* ldsrow = smem + buf * TILE_BYTES + (kw * 64 + cb * 32 + l32) * ROWB;
-    if constexpr (PRELOAD) {
-      typename M::frag bf[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) bf[ks] = M::load_b(ldsrow, ks, half);
+    for (int ks = 0; ks < NKS; ++ks) bf[ks] = M::load_b(ldsrow, ks, half);
+  };
+  auto mfma_block = [&](const frag_t* bf, int buf, int cb) {
+    if constexpr (PRELOAD) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
           acc[rb][cb] = M::mma(afrag[rb][ks], bf[ks], ks == 0 ? f32x16{} : acc[rb][cb]);
     } else {
+      const char* ldsrow = smem + buf * TILE_BYTES + (kw * 64 + cb * 32 + l32) * ROWB;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const typename M::frag bf = M::load_b(ldsrow, ks, half);
+        const frag_t b1 = M::load_b(ldsrow, ks, half);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-          acc[rb][cb] = M::mma(afrag[rb][ks], bf, ks == 0 ? f32x16{} : acc[rb][cb]);
+          acc[rb][cb] = M::mma(afrag[rb][ks], b1, ks == 0 ? f32x16{} : acc[rb][cb]);
       }
     }
   };
-  constexpr int NDSR = NKS * (int)(sizeof(typename M::frag) / 16);  // 16-byte LDS reads per block
-  // the block's fragment reads first, then one MFMA per few VALU ops
-#define IDX_INTERLEAVE(id)                                               \
-  if constexpr (PRELOAD) {                                               \
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NDSR, id);        \
-    _Pragma("unroll") for (int i_ = 0; i_ < 2 * NKS; ++i_) {             \
-      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, id);           \
-      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, id);           \
-    }                                                                    \
+  constexpr int NDSR = NKS * (int)(sizeof(frag_t) / 16);  // 16-byte LDS reads per block
+  // one MFMA per few VALU ops, optionally with the next block's fragment reads spread in
+#define IDX_INTERLEAVE(id, reads)                                                      \
+  if constexpr (PRELOAD) {                                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 2 * NKS; ++i_) {                           \
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, id);                         \
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, 4, id);                         \
+      if ((reads) && i_ < NDSR) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, id); \
+    }                                                                                  \
   }
+
 
   // ---- epilogue of one block: ReLU, x w, sum over heads, scale, mask, store ----
   // The head sum is an in-lane weighted sum over the 16 result rows the lane
   // holds, plus the other half-wave's partial (v_permlane32_swap).  Lanes
   // 0-31 store column block 0 and lanes 32-63 block 1; `key`/`scale` describe
   // this lane's column (kw*64 + half*32 + lane%32) of tile c0.
-  auto epilogue = [&](int cb, int c0, int key, float scale) {
+  auto epilogue = [&](int cb, int c0, int key, float scale, bool live) {
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
       float p0 = 0.f, p1 = 0.f;
@@ -298,11 +332,63 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       const float tot = p + other;
       const int t = t_first + qi;
       const int col = c0 + kw * 64 + half * 32 + l32;
-      if (half == cb && t < r_end && col < c_end) {
-        const bool ok = key >= 0 && key <= row_limit(a, t);
-        const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
-        a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
+      const bool mine = live && half == cb && t < r_end && col < c_end;
+      const bool ok = mine && key >= 0 && key <= row_limit(a, t);
+      const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
+      if constexpr (!FILTER) {
+        if (mine) a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
+      } else {
+        // Running threshold: f_theta is a bin with at least topk counted
+        // scores at or above it, so its lower edge f_lo bounds the row's final
+        // k-th score from below and a score under it cannot be in the top-k.
+        // Only passing scores are counted: bins under the threshold are never
+        // consulted again.
+        if (!f_based) {
+          uint32_t m = ok ? order_key(val) : 0u;
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+          if (m != 0u) {
+            f_base = (int)(m >> 15) - (kFiltBins - 512);
+            f_based = true;
+          }
+        }
+        const bool pass = ok && val >= f_lo;
+        const unsigned long long pm = __ballot(pass);
+        if (pm) {
+          if (pass) {
+            const int bin = min(max((int)(order_key(val) >> 15) - f_base, 0), kFiltBins - 1);
+            atomicAdd(&hist[bin], 1u);
+            const unsigned long long lt = (l == 0) ? 0ull : (~0ull >> (kWave - l));
+            const int off = f_cnt + __popcll(pm & lt);
+            f_val[off] = val;
+            f_idx[off] = key;
+          }
+        }
+        const int np = __popcll(pm);
+        f_cnt += np;
+        f_above += np;
       }
+    }
+  };
+
+  // Raise the threshold bin: advance over the lowest bins at or above it while
+  // at least topk counted scores remain above them.  One gather of 64 bins,
+  // a wave prefix sum and a ballot move it up to 64 bins at a time.  Called
+  // every few tiles: a stale threshold only admits extra candidates.
+  auto advance_theta = [&]() {
+    for (;;) {
+      const int bi = f_theta + l;
+      const int h = bi < kFiltBins ? (int)hist[bi] : 0;
+      const int incl = wave_incl_scan(h);
+      const unsigned long long mv = __ballot(bi < kFiltBins - 1 && f_above - incl >= a.topk);
+      const int J = __popcll(mv);  // a prefix of the lanes: incl is nondecreasing
+      if (J == 0) break;
+      f_above -= __builtin_amdgcn_readlane(incl, J - 1);
+      f_theta += J;
+      // smallest key of bin f_theta (bins above 0 start at (f_theta + f_base) << 15;
+      // a non-positive start means every key lies at or above it)
+      f_lo = (f_theta + f_base) > 0 ? key_to_float((uint32_t)(f_theta + f_base) << 15) : neg_inf();
+      if (J < kWave) break;
     }
   };
 
@@ -311,15 +397,22 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   // (of this tile or of the previous one) executes on the VALU; the next
   // tile's global loads are in flight meanwhile, and one barrier per tile
   // publishes the next LDS buffer.
-  stage_load(c_begin);
-  stage_store(0);
+  // Global loads run two tiles ahead of the MFMAs (two register staging sets;
+  // set P holds the tiles of parity P between their load and their store).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  stage_load(S0{}, c_begin);
+  if (c_begin + TW < c_end) stage_load(S1{}, c_begin + TW);
+  stage_store(S0{}, 0);
   __syncthreads();
-  int buf = 0, prev_c0 = -1, key_prev = -1;
+  int buf = 0, prev_c0 = c_begin, key_prev = -1;
   float scale_prev = 1.f;
   const int jl = kw * 64 + half * 32 + l32;
-  for (int c0 = c_begin; c0 < c_end; c0 += TW) {
-    const bool has_next = c0 + TW < c_end;
-    if (has_next) stage_load(c0 + TW);
+  auto tile = [&](auto par_c, int c0) {
+    constexpr int PAR = decltype(par_c)::value;  // parity of this tile's index
+    using Cur = std::integral_constant<int, PAR>;
+    using Nxt = std::integral_constant<int, 1 - PAR>;
+    if (c0 + 2 * TW < c_end) stage_load(Cur{}, c0 + 2 * TW);
     int key_cur = c0 + jl;
     float scale_cur = 1.f;
     if (COLINFO) {
@@ -327,40 +420,63 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
       key_cur = ck[jl];
       scale_cur = ((const float*)(ck + TW))[jl];
     }
-    mfma_block(buf, 0);
-    if (prev_c0 >= 0) epilogue(1, prev_c0, key_prev, scale_prev);
-    IDX_INTERLEAVE(0);
-    mfma_block(buf, 1);
-    epilogue(0, c0, key_cur, scale_cur);
-    IDX_INTERLEAVE(1);
-    if (has_next) stage_store(buf ^ 1);
+    if constexpr (PRELOAD) load_block(bfA, buf, 0);
+    // block 0 MFMAs || block 1 epilogue of the previous tile (nothing is
+    // stored on the first tile) || block 1 fragment reads
+    mfma_block(bfA, buf, 0);
+    epilogue(1, prev_c0, key_prev, scale_prev, c0 != c_begin);
+    if constexpr (PRELOAD) load_block(bfB, buf, 1);
+    IDX_INTERLEAVE(0, true);
+    // block 1 MFMAs || block 0 epilogue
+    mfma_block(bfB, buf, 1);
+    epilogue(0, c0, key_cur, scale_cur, true);
+    IDX_INTERLEAVE(1, false);
+    if constexpr (FILTER) {
+      if ((((c0 - c_begin) / TW) & 3) == 3) advance_theta();
+    }
+    if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
     __syncthreads();
     prev_c0 = c0;
     key_prev = key_cur;
     scale_prev = scale_cur;
     buf ^= 1;
+  };
+  for (int c0 = c_begin; c0 < c_end; c0 += 2 * TW) {
+    tile(S0{}, c0);
+    if (c0 + TW < c_end) tile(S1{}, c0 + TW);
   }
-  if (prev_c0 >= 0) epilogue(1, prev_c0, key_prev, scale_prev);
+  epilogue(1, prev_c0, key_prev, scale_prev, true);
+  if constexpr (FILTER) {
+    if (l == 0 && t_first < r_end) a.ccount[(long long)b * a.n_rows + t_first - a.row0] = f_cnt;
+  }
 #undef IDX_INTERLEAVE
 }
 
-template <int QF, int KF, int H, int D, int RW, bool GATHER>
+template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER = false>
 static hipError_t launch_mode(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D, RW, GATHER>,
+    hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D, RW, GATHER, NWV, FILTER>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((score_kernel<QF, KF, H, D, RW, GATHER>), grid, dim3(kScoreThreads), lds, st, a);
+  hipLaunchKernelGGL((score_kernel<QF, KF, H, D, RW, GATHER, NWV, FILTER>), grid, dim3(NWV * 64), lds, st, a);
   return hipGetLastError();
 }
 
+// Workgroups of 8 waves, or of 4 row-waves (two independent workgroups per CU).
 template <int QF, int KF, int H, int D, int RW>
 static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
-  if (a.mode == kModeGather) return launch_mode<QF, KF, H, D, RW, true>(a, grid, lds, st);
-  return launch_mode<QF, KF, H, D, RW, false>(a, grid, lds, st);
+  const bool g = a.mode == kModeGather;
+  if constexpr (H == 64 && RW == 8) {
+    if (a.filter && !g) return launch_mode<QF, KF, H, D, 8, false, 8, true>(a, grid, lds, st);
+  }
+  if (RW == 4 && a.nw == 4)
+    return g ? launch_mode<QF, KF, H, D, 4, true, 4>(a, grid, lds, st)
+             : launch_mode<QF, KF, H, D, 4, false, 4>(a, grid, lds, st);
+  return g ? launch_mode<QF, KF, H, D, RW, true, 8>(a, grid, lds, st)
+           : launch_mode<QF, KF, H, D, RW, false, 8>(a, grid, lds, st);
 }
 
 template <int QF, int KF, int H, int D>
@@ -386,17 +502,19 @@ static hipError_t pick_h(const ScoreArgs& a, int H, int D, dim3 grid, size_t lds
   return hipErrorInvalidValue;
 }
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw) {
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter) {
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
-  const int tw = (kScoreThreads / kWave / rw) * 64;
+  const int tw = (nw / rw) * 64;
   (void)kf;
-  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8);  // double-buffered tiles
+  // double-buffered tiles, then one filtering histogram per wave
+  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) +
+         (filter ? (size_t)nw * kFiltBins * 4 : 0);
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st) {
   dim3 grid(a.n_blocks, n_col_chunks);
-  const size_t lds = score_lds_bytes(qf, kf, D, a.rw);
+  const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter);
   if (qf == F32 && kf == F32) return pick_h<F32, F32>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == BF16) return pick_h<BF16, BF16>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == FP8) return pick_h<BF16, FP8>(a, H, D, grid, lds, st);

@@ -49,15 +49,11 @@ struct SelectShared {
 };
 
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
+  if (a.mode == kModeList) return min(a.counts[blockIdx.x], a.n_cols);
   if (a.mode == kModeGather) return a.n_cols;
   const int lim = (a.mode == kModeProxy) ? a.q_pos0 + min((r + 1) * a.group, a.n_q) - 1
                                          : a.q_pos0 + r;
   return min(lim + 1, a.n_cols);
-}
-
-// Inverse of order_key (for eligible keys).
-__device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 __device__ __forceinline__ uint32_t load_key(const float* row, int c) {
@@ -102,27 +98,42 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     const int n_g = (a.n_q + a.group - 1) / a.group;
     crow = a.cand + ((long long)b * n_g + r / a.group) * a.n_cols;
   }
+  if (a.mode == kModeList) crow = a.lidx + (long long)blockIdx.x * a.ld;
   const int len = row_length(a, r);
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
   constexpr int REG = KPT > 0 ? KPT : 1;
   uint32_t keys[REG];
+  // rows longer than the register tile (possible for candidate lists) stream
+  const bool regs = KPT > 0 && len <= REG * kSelectThreads;
 
-  auto idx_at = [&](int c) -> int { return crow ? crow[c] : c; };
+  // Rows with their own key indices (gather, list) keep the indices beside the
+  // keys (registers, or batched loads when streaming): no dependent loads
+  // later.  Otherwise the key index is the column.
+  const bool indexed = crow != nullptr;
+  int idxs[REG];
   auto key_at = [&](int c) -> uint32_t { return load_key(row, c); };
-  // Calls f(column, key) for every column of this thread (eligible or not).
+  // Calls f(column, key, key index) for every column of this thread (eligible or not).
   auto for_keys = [&](auto&& f) {
-    if (KPT > 0) {
+    if (KPT > 0 && regs) {
 #pragma unroll
-      for (int i = 0; i < REG; ++i) f(i * kSelectThreads + tid, keys[i]);
+      for (int i = 0; i < REG; ++i) {
+        const int c = i * kSelectThreads + tid;
+        f(c, keys[i], indexed ? idxs[i] : c);
+      }
     } else {
       for (int c0 = 0; c0 < len; c0 += 8 * kSelectThreads) {
         float v[8];
+        int x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = row[min(c0 + j * kSelectThreads + tid, len - 1)];
+        for (int j = 0; j < 8; ++j) {
+          const int cc = min(c0 + j * kSelectThreads + tid, max(len - 1, 0));
+          v[j] = row[cc];
+          x[j] = indexed ? crow[cc] : cc;
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int c = c0 + j * kSelectThreads + tid;
-          f(c, (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded);
+          f(c, (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded, x[j]);
         }
       }
     }
@@ -131,18 +142,22 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   // ---- 1. load (batched, clamped addresses), count, min, max ----
   int nv = 0;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  if (KPT > 0) {
+  if (KPT > 0 && regs) {
     // every load of the row at once (clamped addresses: no per-element branch)
     float v[REG];
 #pragma unroll
-    for (int i = 0; i < REG; ++i) v[i] = row[min(i * kSelectThreads + tid, len - 1)];
+    for (int i = 0; i < REG; ++i) {
+      const int cc = min(i * kSelectThreads + tid, max(len - 1, 0));
+      v[i] = row[cc];
+      if (indexed) idxs[i] = crow[cc];
+    }
 #pragma unroll
     for (int i = 0; i < REG; ++i) {
       const int c = i * kSelectThreads + tid;
       keys[i] = (c < len && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
     }
   }
-  for_keys([&](int, uint32_t k) {
+  for_keys([&](int, uint32_t k, int) {
     if (k != kKeyExcluded) {
       ++nv;
       kmin = min(kmin, k);
@@ -221,7 +236,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       };
       for (int i = tid; i < kBins; i += kSelectThreads) sh.hist[i] = 0;
       __syncthreads();
-      for_keys([&](int, uint32_t k) {
+      for_keys([&](int, uint32_t k, int) {
         if (k != kKeyExcluded) atomicAdd(&sh.hist[lbin(k)], 1u);
       });
       __syncthreads();
@@ -232,7 +247,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       in_bin = (int)sh.hist[b];
       // the key range of that bin
       uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      for_keys([&](int, uint32_t k) {
+      for_keys([&](int, uint32_t k, int) {
         if (k != kKeyExcluded && lbin(k) == b) {
           mn = min(mn, k);
           mx = max(mx, k);
@@ -267,7 +282,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
       for (int i = tid; i < kBins; i += kSelectThreads) sh.hist[i] = 0;
       __syncthreads();
       const uint32_t lo = blo, hi = bhi;
-      for_keys([&](int, uint32_t k) {
+      for_keys([&](int, uint32_t k, int) {
         if (k != kKeyExcluded && k >= lo && k <= hi) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
       });
       __syncthreads();
@@ -289,11 +304,11 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         if (tid == 0) sh.list_n = 0;
         __syncthreads();
         const uint32_t lo = blo, hi = bhi;
-        for_keys([&](int c, uint32_t k) {
+        for_keys([&](int, uint32_t k, int ix) {
           if (k != kKeyExcluded && k >= lo && k <= hi) {
             const int slot = atomicAdd(&sh.list_n, 1);
             sh.lkey[slot] = k;
-            sh.lidx[slot] = idx_at(c);
+            sh.lidx[slot] = ix;
           }
         });
         __syncthreads();
@@ -318,9 +333,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
         for (int shift = 24; shift >= 0; shift -= 8) {
           for (int i = tid; i < 256; i += kSelectThreads) sh.bins256[i] = 0;
           __syncthreads();
-          for_keys([&](int c, uint32_t k) {
+          for_keys([&](int, uint32_t k, int ixv) {
             if (k == tau) {
-              const uint32_t ix = (uint32_t)idx_at(c);
+              const uint32_t ix = (uint32_t)ixv;
               if ((ix & im) == ip) atomicAdd(&sh.bins256[(ix >> shift) & 255u], 1u);
             }
           });
@@ -355,20 +370,20 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     return k != kKeyExcluded && (k > cut_hi || (whole && k >= cut_lo));
   };
   int mine = 0;
-  for_keys([&](int, uint32_t k) { mine += certain(k); });
+  for_keys([&](int, uint32_t k, int) { mine += certain(k); });
   int total;
   int off = block_excl_scan<NT>(mine, &total, sh);
-  for_keys([&](int c, uint32_t k) {
-    if (certain(k)) out[off++] = idx_at(c);
+  for_keys([&](int, uint32_t k, int ix) {
+    if (certain(k)) out[off++] = ix;
   });
   if (idx_radix) {
     const uint32_t tau = blo;
     int tmine = 0;
-    for_keys([&](int c, uint32_t k) { tmine += (k == tau && idx_at(c) <= idx_thr); });
+    for_keys([&](int, uint32_t k, int ix) { tmine += (k == tau && ix <= idx_thr); });
     int ttot;
     int toff = above + block_excl_scan<NT>(tmine, &ttot, sh);
-    for_keys([&](int c, uint32_t k) {
-      if (k == tau && idx_at(c) <= idx_thr) out[toff++] = idx_at(c);
+    for_keys([&](int, uint32_t k, int ix) {
+      if (k == tau && ix <= idx_thr) out[toff++] = ix;
     });
   }
   for (int i = kk + tid; i < topk; i += kSelectThreads) out[i] = -1;
@@ -392,6 +407,8 @@ static hipError_t launch_by_length(const SelectArgs& a, int rows, int n, hipStre
 // sequence; such launches are split into length classes so that each class
 // runs the smallest variant that holds its rows.
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st) {
+  // candidate lists are mostly short; a longer list streams inside the kernel
+  if (a.mode == kModeList) return launch_kpt<512, 16>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
   const int classes[4] = {256 * 8, 512 * 16, 1024 * 16, 1024 * 32};
   long long r = 0;

@@ -50,7 +50,7 @@ class Workload:
     group: int = 0      # 0: dense only
     n_cand: int = 0
     seed: int = 0
-    w_dist: str = "uniform"  # "uniform" | "int"
+    w_dist: str = "uniform"  # "uniform" | "int" | "signed" (U(-1, 1): scores can be negative)
 
     @property
     def q_pos0(self):
@@ -142,6 +142,8 @@ def make_inputs(wl: Workload, device="cpu"):
     w = torch.rand((B, nq, H), generator=g, device=device, dtype=torch.float32)
     if wl.w_dist == "int":
         w = torch.floor(w * 3.0)
+    elif wl.w_dist == "signed":
+        w = 2.0 * w - 1.0
     qs, q_scale = _store(q, wl.q_fmt, (2, 3))
     del q
     ks, k_scale = _store(k, wl.k_fmt, (2,))

@@ -105,10 +105,15 @@ def test_workspace_sizes_follow_the_layout(lib):
     p = problem(n_q=1000, n_k=1000)
     need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 8)
     assert need >= 1000 * 1000 * 4 and need % 256 == 0
-    # large: capped near 1 GiB of buffered rows
+    # large: about 1 GiB-worth of buffered score rows; with 64 heads the rows
+    # are candidate lists (score + key per slot, plus a count): twice that
     big = problem(n_q=131072, n_k=131072)
     nb = lib.idx_workspace_bytes(ctypes.byref(big), 0, 0, 0, 2048)
-    assert (1 << 30) <= nb <= (1 << 30) + 8 * 131072 * 4 + 256
+    rows = (1 << 30) // (131072 * 4)
+    assert nb >= rows * (131072 * 8 + 4) and nb <= (rows + 8) * (131072 * 8 + 4) + 256
+    big32 = problem(n_q=131072, n_k=131072, heads=32)
+    nb32 = lib.idx_workspace_bytes(ctypes.byref(big32), 0, 0, 0, 2048)
+    assert (1 << 30) <= nb32 <= (1 << 30) + 16 * 131072 * 4 + 256
     # proxy scan: proxy q (bf16) + proxy w + score rows
     g = lib.idx_workspace_bytes(ctypes.byref(p), 1, 10, 64, 0)
     assert g >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + 100 * 1000 * 4
