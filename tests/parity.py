@@ -66,7 +66,7 @@ def check_scores(gpu, ref, what=""):
 
 
 def sets(rows):
-    return [frozenset(int(x) for x in r if x >= 0) for r in np.asarray(rows)]
+    return [frozenset(int(x) for x in np.asarray(r).ravel() if x >= 0) for r in rows]
 
 
 def assert_same_sets(a, b, what=""):
