@@ -168,6 +168,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of 1 GiB (4 times): the known-size reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings to HBM bytes")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -177,6 +180,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = 1 << 28  # float32 elements: 1 GiB read + 1 GiB written per copy
+        x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(4):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": 4 * n,
+                          "bytes_written_per_copy": 4 * n, "copies": 4}))
+        return
     import sparse_attention_token_causal_amd as S
     from sparse_attention_token_causal_amd.synth import WORKLOADS, make_inputs
 
