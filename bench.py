@@ -74,12 +74,29 @@ def measured_traffic(workload):
 def make_step(S, wl, inp, dev):
     """Returns (step(), pairs_per_step, flops_per_step, queries_per_step, dtype, kind)."""
     import torch
+    from sparse_attention_token_causal_amd.synth import make_inputs
 
     H, d = wl.heads, wl.dim
     a = dict(q_scale=inp["q_scale"], k_scale=inp["k_scale"], q_pos0=wl.q_pos0)
     dense_pairs = wl.batch * causal_pairs(wl.n_q, wl.n_k, wl.q_pos0)
     dtype = "fp8" if wl.q_fmt == "fp8" else ("f32" if wl.q_fmt == "f32" else "bf16")
     if wl.group == 0 or wl.name.startswith("decode") or wl.name.startswith("prefill"):
+        if wl.n_q < wl.n_k:
+            # decode: the key cache (134 MB) fits the 256 MB Infinity Cache, so the
+            # steps rotate over four independent caches (>= 540 MB) to time HBM reads
+            sets = [inp] + [make_inputs(wl.scaled(seed=wl.seed + i), dev) for i in range(1, 4)]
+            outs = [torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device=dev) for _ in sets]
+            p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
+            ws = torch.empty(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk), dtype=torch.uint8,
+                             device=dev)
+            it = [0]
+
+            def step():
+                x = sets[it[0] % len(sets)]
+                S.score_topk(x["q"], x["k"], x["w"], wl.topk, q_scale=x["q_scale"], k_scale=x["k_scale"],
+                             q_pos0=wl.q_pos0, workspace=ws, out=outs[it[0] % len(sets)])
+                it[0] += 1
+            return step, dense_pairs, dense_pairs * 2 * H * d, wl.batch * wl.n_q, dtype, "decode"
         p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
         # a workspace for every row at once (score rows, or candidate lists of
         # (score, key) slots and a count): one score and one select launch per step

@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "kernels.hpp"
@@ -158,8 +159,15 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     const long long r0 = block_start_row(L.mode, blk0, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
     const long long r1 = block_start_row(L.mode, blk0 + nb, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
     if (r1 <= r0) continue;
+    // Split the key columns when there are few row blocks: aim for about two
+    // workgroups per CU with at least 16 key tiles each (long scans such as
+    // decode), and for at least one per CU on short scans.  Filtering keeps
+    // whole rows in one workgroup.
     int chunks = 1;
-    if (nb < 1024 && !flt.on) chunks = ceil_div(2048, nb);  // filtering keeps whole rows
+    if (nb < 512 && !flt.on) {
+      chunks = std::max(1, std::min(ceil_div(512, nb), ceil_div(L.n_cols, 16 * tw)));
+      if ((long long)nb * chunks < 256) chunks = std::min(ceil_div(256, nb), ceil_div(L.n_cols, tw));
+    }
     int kc = ceil_div(L.n_cols, chunks);
     kc = ceil_div(kc, tw) * tw;
     chunks = ceil_div(L.n_cols, kc);
@@ -179,7 +187,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.topk = topk;
     if (timed(IDX_KERNEL_SCORE, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
       return IDX_EHIP;
-    SelectArgs se;
+    SelectArgs se = {};
     se.scores = buf + (full ? r0 * (long long)L.n_cols : 0);
     se.ld = L.n_cols;
     se.row0 = r0;
@@ -240,6 +248,135 @@ size_t proxy_q_bytes(const idx_problem* p, int n_g) {
   return (size_t)p->batch * n_g * p->heads * p->dim * (proxy_q_dtype(p) == IDX_F32 ? 4 : 2);
 }
 
+
+// Short row sets (at most kSplitMaxRows queries or proxies per sequence, the
+// decode shape) take the split-key scan with the histogram / compaction /
+// list select.  `qf` is the format the scan reads q in.
+bool split_shape(const idx_problem* p, int n_rows, int qf) {
+  return n_rows <= kSplitMaxRows && qf != IDX_F32 && p->k_dtype != IDX_F32;
+}
+
+// Key chunks of the split-key scan: about two workgroups per CU in one round.
+int split_kc(const idx_problem* p) {
+  const int chunks = std::max(1, std::min(ceil_div(512, p->batch), ceil_div(p->n_k, 128)));
+  return ceil_div(ceil_div(p->n_k, chunks), 128) * 128;
+}
+
+// Compaction segments: about 512 workgroups over all rows, at most kMaxSegs per row.
+int split_seg(const idx_problem* p, int n_rows) {
+  const int R = p->batch * n_rows;
+  int seg = std::max(1024, ceil_div(ceil_div(p->n_k, ceil_div(512, R)), 256) * 256);
+  if (ceil_div(p->n_k, seg) > kMaxSegs) seg = ceil_div(ceil_div(p->n_k, kMaxSegs), 256) * 256;
+  return seg;
+}
+
+struct SplitLayout {
+  int kc, chunks, seg, segs;
+  size_t scores, win, wbase, cval, cidx, segcnt, gval, gidx, total;  // byte offsets
+};
+
+// Region, R = B * n_rows: [R, n_k] scores | [R, chunks, kSplitWin] windows |
+// [R, chunks] window bases | [R, n_k] candidate scores | [R, n_k] candidate
+// keys | [R, segs] segment counts | [R, n_k] gathered scores | [R, n_k]
+// gathered keys.
+SplitLayout split_layout(const idx_problem* p, int n_rows) {
+  const size_t R = (size_t)p->batch * n_rows, row = (size_t)p->n_k * 4;
+  SplitLayout s;
+  s.kc = split_kc(p);
+  s.chunks = ceil_div(p->n_k, s.kc);
+  s.seg = split_seg(p, n_rows);
+  s.segs = ceil_div(p->n_k, s.seg);
+  size_t o = 0;
+  s.scores = o;  o += align_up(R * row);
+  s.win = o;     o += align_up(R * s.chunks * kSplitWin * 4);
+  s.wbase = o;   o += align_up(R * s.chunks * 4);
+  s.cval = o;    o += align_up(R * row);
+  s.cidx = o;    o += align_up(R * row);
+  s.segcnt = o;  o += align_up(R * s.segs * 4);
+  s.gval = o;    o += align_up(R * row);
+  s.gidx = o;    o += align_up(R * row);
+  s.total = o;
+  return s;
+}
+
+// Split-key scan of n_rows rows per sequence, then the top-`topk` of each row
+// into out [B * n_rows, topk].  `scores` (if non-null) receives the scores
+// (already filled with -inf by the caller); otherwise the region's own
+// buffer holds them.
+int split_score_select(const idx_problem* p, int qf, const void* q, const float* q_scale,
+                       const float* w, int n_rows, int mode, int group, int topk, int* out,
+                       float* scores, char* region, hipStream_t st) {
+  const SplitLayout sl = split_layout(p, n_rows);
+  const int B = p->batch, R = B * n_rows;
+  if (!scores) scores = (float*)(region + sl.scores);
+  SplitArgs a = {};
+  a.q = q;
+  a.q_scale = q_scale;
+  a.k = p->k;
+  a.k_scale = p->k_scale;
+  a.w = w;
+  a.n_rows = n_rows;
+  a.n_k = p->n_k;
+  a.n_q = p->n_q;
+  a.q_pos0 = p->q_pos0;
+  a.group = group;
+  a.mode = mode;
+  const int waves = ceil_div((long long)n_rows * p->heads, 64);
+  a.rwn = waves <= 1 ? 1 : (waves <= 2 ? 2 : 4);
+  a.kc = sl.kc;
+  a.out = scores;
+  a.win = (uint32_t*)(region + sl.win);
+  a.wbase = (int*)(region + sl.wbase);
+  a.n_chunks = sl.chunks;
+  if (timed(IDX_KERNEL_SCORE, st, [&] {
+        return launch_split_scan(a, qf, p->k_dtype, p->heads, p->dim, B, sl.chunks, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  CompactArgs c = {};
+  c.scores = scores;
+  c.win = a.win;
+  c.wbase = a.wbase;
+  c.n_chunks = sl.chunks;
+  c.n_rows = n_rows;
+  c.n_k = p->n_k;
+  c.n_q = p->n_q;
+  c.q_pos0 = p->q_pos0;
+  c.group = group;
+  c.mode = mode;
+  c.topk = topk;
+  c.seg = sl.seg;
+  c.n_segs = sl.segs;
+  c.cval = (float*)(region + sl.cval);
+  c.cidx = (int*)(region + sl.cidx);
+  c.segcnt = (int*)(region + sl.segcnt);
+  SelectArgs se = {};
+  se.scores = c.cval;
+  se.ld = p->n_k;
+  se.row0 = 0;
+  se.n_rows = n_rows;
+  se.n_cols = p->n_k;
+  se.mode = kModeList;
+  se.q_pos0 = p->q_pos0;
+  se.n_q = p->n_q;
+  se.group = group;
+  se.lidx = c.cidx;
+  se.seg_counts = c.segcnt;
+  se.n_segs = sl.segs;
+  se.seg_len = sl.seg;
+  se.gval = (float*)(region + sl.gval);
+  se.gidx = (int*)(region + sl.gidx);
+  se.topk = topk;
+  se.out = out;
+  // lists hold the rows' top-k plus the rest of the threshold bin
+  const int expect = (int)std::min<long long>(p->n_k, 8LL * topk);
+  if (timed(IDX_KERNEL_SELECT, st, [&] {
+        hipError_t e = launch_split_compact(c, R, st);
+        return e != hipSuccess ? e : launch_select_list(se, R, expect, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  return IDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,15 +400,17 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
   if (op == IDX_OP_REUSE_TOPK) return 0;
   if (check_problem(p) != IDX_OK) return 0;
   if (op == IDX_OP_SCORE_TOPK) {
+    if (split_shape(p, p->n_q, p->q_dtype)) return split_layout(p, p->n_q).total;
     Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
     return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * score_row_bytes(p, L));
   }
   if (group < 1) return 0;
   const int n_g = ceil_div(p->n_q, group);
   if (op == IDX_OP_GROUP_PROXY_SCAN) {
+    const size_t proxy = align_up(proxy_q_bytes(p, n_g)) + align_up((size_t)p->batch * n_g * p->heads * 4);
+    if (split_shape(p, n_g, proxy_q_dtype(p))) return proxy + split_layout(p, n_g).total;
     Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
-    return align_up(proxy_q_bytes(p, n_g)) + align_up((size_t)p->batch * n_g * p->heads * 4) +
-           align_up((size_t)buffer_rows(L, (long long)p->batch * n_g) * p->n_k * 4);
+    return proxy + align_up((size_t)buffer_rows(L, (long long)p->batch * n_g) * p->n_k * 4);
   }
   if (op == IDX_OP_REFINE_TOPK) {
     if (n_cand < 1) return 0;
@@ -287,10 +426,20 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
   if (rc != IDX_OK) return rc;
   if (topk < 1 || !out_idx) return IDX_EINVAL;
   hipStream_t st = (hipStream_t)stream;
+  const bool full = out_scores != nullptr;
+  if (split_shape(p, p->n_q, p->q_dtype)) {
+    const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
+    if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+    if (full && timed(IDX_KERNEL_FILL, st, [&] {
+          return launch_fill(out_scores, (size_t)p->batch * p->n_q * p->n_k, -__builtin_huge_valf(), st);
+        }) != hipSuccess)
+      return IDX_EHIP;
+    return split_score_select(p, p->q_dtype, p->q, p->q_scale, p->w, p->n_q, kModeDense, 1, topk,
+                              out_idx, out_scores, (char*)ws, st);
+  }
   Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
   float* buf;
   long long rows;
-  const bool full = out_scores != nullptr;
   if (full) {
     buf = out_scores;
     rows = (long long)p->batch * p->n_q;
@@ -341,8 +490,16 @@ int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand
                                   p->q_dtype, group, pq, pw, st);
       }) != hipSuccess)
     return IDX_EHIP;
-  Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
   const bool full = out_proxy_scores != nullptr;
+  if (split_shape(p, n_g, pqf)) {
+    if (full && timed(IDX_KERNEL_FILL, st, [&] {
+          return launch_fill(out_proxy_scores, (size_t)p->batch * n_g * p->n_k, -__builtin_huge_valf(), st);
+        }) != hipSuccess)
+      return IDX_EHIP;
+    return split_score_select(p, pqf, pq, nullptr, pw, n_g, kModeProxy, group, n_cand, out_cand,
+                              out_proxy_scores, cur, st);
+  }
+  Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
   float* buf;
   long long rows;
   if (full) {

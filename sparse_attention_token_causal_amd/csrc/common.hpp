@@ -46,13 +46,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 // Four OCP E4M3 codes (one dword) -> four bfloat16 values packed in two
-// dwords (low code first).  The hardware conversion yields exact float32
-// values; E4M3 has 3 mantissa bits, so the bfloat16 truncation is exact.
+// dwords (low code first).  gfx950's packed conversion (scale 1.0) is exact:
+// E4M3 has 3 mantissa bits and a narrower exponent range than bfloat16.
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t codes, uint32_t& lo, uint32_t& hi) {
-  auto a = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);  // codes 0,1
-  auto b = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);   // codes 2,3
-  lo = bf16_hi(a[0]) | (bf16_hi(a[1]) << 16);
-  hi = bf16_hi(b[0]) | (bf16_hi(b[1]) << 16);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
 }
 
 __device__ __forceinline__ float fp8_to_f32(uint32_t code) {

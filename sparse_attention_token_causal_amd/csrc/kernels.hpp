@@ -58,6 +58,14 @@ struct SelectArgs {
   const int* cand;        // gather: key index of each column
   const int* lidx;        // list: key indices, same layout as scores
   const int* counts;      // list: entries per launch row
+  // segmented list (when seg_counts is set; counts is then unused): launch
+  // row i holds seg_counts[i * n_segs + s] entries of segment s at
+  // scores/lidx + i * ld + s * seg_len; they are gathered into gval/gidx
+  // (same row layout) before the select
+  const int* seg_counts;
+  int n_segs, seg_len;
+  float* gval;
+  int* gidx;
   int topk;
   int* out;               // [B * n_rows, topk], indexed by flattened row
 };
@@ -66,6 +74,48 @@ size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter);
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st);
+// Split-key scan (few rows per sequence, long key axis): see split.hip.
+constexpr int kSplitBins = 4096;   // per-row histogram of the top 12 order-key bits
+constexpr int kSplitWin = 128;     // histogram bins a scan workgroup reports per row
+constexpr int kSplitMaxRows = 4;   // rows (queries or proxies) per sequence
+constexpr int kMaxSegs = 256;      // segments of a segmented list
+
+struct SplitArgs {
+  const void* q;          // [B, n_rows, H, D]
+  const float* q_scale;   // [B, n_rows] (FP8 q only)
+  const void* k;          // [B, n_k, D]
+  const float* k_scale;   // [B, n_k] (FP8 k only)
+  const float* w;         // [B, n_rows, H]
+  int n_rows, n_k, n_q, q_pos0, group, mode;  // mode: kModeDense or kModeProxy
+  int rwn;                // 64-row waves per workgroup for the rows (1, 2 or 4)
+  int kc;                 // key columns per workgroup (grid.x = ceil(n_k / kc))
+  float* out;             // [B * n_rows, n_k] scores (-inf: masked)
+  // per (row, chunk): the chunk's histogram bins [wbase, wbase + kSplitWin)
+  // of that row, wbase = max(top non-empty bin - kSplitWin + 1, 0), or -1
+  // when the chunk holds no eligible score of the row
+  uint32_t* win;          // [B * n_rows, n_chunks, kSplitWin]
+  int* wbase;             // [B * n_rows, n_chunks]
+  int n_chunks;
+};
+
+struct CompactArgs {
+  const float* scores;    // [B * n_rows, n_k]
+  const uint32_t* win;    // as SplitArgs
+  const int* wbase;
+  int n_chunks;
+  int n_rows, n_k, n_q, q_pos0, group, mode, topk;
+  int seg;                // columns per workgroup (grid.x = n_segs = ceil(n_k / seg))
+  int n_segs;
+  float* cval;            // [B * n_rows, n_k]: segment s's candidates from s * seg
+  int* cidx;              // [B * n_rows, n_k] their key indices
+  int* segcnt;            // [B * n_rows, n_segs] candidates per segment
+};
+
+hipError_t launch_split_scan(const SplitArgs& a, int qf, int kf, int H, int D, int B, int chunks,
+                             hipStream_t st);
+hipError_t launch_split_compact(const CompactArgs& a, int rows, hipStream_t st);
+// List select with a row-length hint (the variant that keeps that many keys in registers).
+hipError_t launch_select_list(const SelectArgs& a, int n_launch_rows, int expect_len, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
 hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* w, int B, int n_q,
                               int H, int D, int qf, int group, void* pq, float* pw,

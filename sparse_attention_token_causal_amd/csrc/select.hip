@@ -46,6 +46,7 @@ struct SelectShared {
   int sel_above;
   // fallback radix state
   uint32_t bins256[256];
+  int soff[kMaxSegs + 1];  // segmented lists: offset of each segment in the gathered list
 };
 
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
@@ -99,8 +100,52 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
     crow = a.cand + ((long long)b * n_g + r / a.group) * a.n_cols;
   }
   if (a.mode == kModeList) crow = a.lidx + (long long)blockIdx.x * a.ld;
-  const int len = row_length(a, r);
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  int len;
+  if (a.mode == kModeList && a.seg_counts) {
+    // Segmented list: segment s of the row holds seg_counts[s] entries from
+    // position s * seg_len.  Gather them, in segment order, into one
+    // contiguous list (gval/gidx) that the rest of the kernel reads.
+    const int ns = a.n_segs;
+    int tot;
+    const int cnt = tid < ns ? a.seg_counts[(long long)blockIdx.x * ns + tid] : 0;
+    const int ex = block_excl_scan<NT>(cnt, &tot, sh);
+    if (tid < ns) sh.soff[tid] = ex;
+    if (tid == 0) sh.soff[ns] = tot;
+    __syncthreads();
+    float* gv = a.gval + (long long)blockIdx.x * a.ld;
+    int* gi = a.gidx + (long long)blockIdx.x * a.ld;
+    for (int c0 = 0; c0 < tot; c0 += 8 * NT) {
+      float v[8];
+      int x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = min(c0 + j * NT + tid, tot - 1);
+        int lo = 0, hi = ns - 1;  // last segment whose offset is <= c
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sh.soff[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const long long src = (long long)lo * a.seg_len + (c - sh.soff[lo]);
+        v[j] = row[src];
+        x[j] = crow[src];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + j * NT + tid;
+        if (c < tot) {
+          gv[c] = v[j];
+          gi[c] = x[j];
+        }
+      }
+    }
+    __syncthreads();
+    row = gv;
+    crow = gi;
+    len = min(tot, a.n_cols);
+  } else {
+    len = row_length(a, r);
+  }
   constexpr int REG = KPT > 0 ? KPT : 1;
   uint32_t keys[REG];
   // rows longer than the register tile (possible for candidate lists) stream
@@ -442,6 +487,10 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
     r = e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_select_list(const SelectArgs& a, int n_launch_rows, int expect_len, hipStream_t st) {
+  return launch_by_length(a, n_launch_rows, expect_len, st);
 }
 
 __global__ void fill_kernel(float* p, size_t n, float v) {

@@ -1,0 +1,434 @@
+// Split-key scan and multi-workgroup select for short row sets on gfx950.
+//
+// In decode each sequence contributes only the few queries of one
+// multi-token-prediction step, but every one of them scans the whole cached
+// key history ("ADIndex Restructures Sparse-Attention Indexing with
+// Group-Level Distillation", "Why the Indexer Becomes the Bottleneck";
+// "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention",
+// Abstract: the decode group is the set of queries of one MTP step).  Such a
+// scan reads far more key bytes than it has query rows to reuse them on, so
+// it is laid out for streaming the keys rather than for tile reuse:
+//
+//  * a workgroup of 4 waves owns one (sequence, key chunk); the sequence's
+//    (query, head) rows - at most 4 queries, 256 rows - are split into
+//    64-row waves whose q fragments stay in registers, and the other waves
+//    of the workgroup take alternate 32-column steps of the chunk;
+//  * no LDS staging: each lane loads the half key row of its own MFMA
+//    column straight into registers.  The head dimension is permuted (the
+//    same way for q and k, which leaves every dot product unchanged) so that
+//    lane half h covers the contiguous half [h*d/2, (h+1)*d/2) of the row;
+//    a ring of P steps keeps several loads per wave in flight;
+//  * FP8 keys under bfloat16 q are widened to bfloat16 in registers (exact);
+//    FP8 x FP8 runs the f8f6f4 MFMA directly;
+//  * the epilogue is the tiled scan's: ReLU, x w (x q scale), head sum in
+//    the lane plus one permlane32 swap, key scale, causal mask.
+//
+// Top-k over rows of 10^5 keys with only a handful of rows needs more than
+// one workgroup per row, and no global atomics (same-address atomics from
+// many workgroups serialize across the chip's XCDs).  Every eligible score
+// also lands in its workgroup's LDS histogram of the top 12 bits of its order
+// key, and each workgroup reports a window of that histogram per row; the
+// compaction kernel (many workgroups per row) sums the windows, finds the bin
+// that holds the row's k-th score and writes every score of its segment in or
+// above that bin to the segment's part of the candidate list; the list select
+// gathers the segments and ranks the candidates exactly (ties to the lower
+// key index).
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <type_traits>
+
+namespace idx {
+
+constexpr int kSplitShift = 32 - 12;  // histogram bin = order key >> kSplitShift
+// gfx9 sched_group_barrier instruction classes
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
+
+__device__ __forceinline__ int split_limit(int mode, int q_pos0, int n_q, int group, int t) {
+  if (mode == kModeProxy) return q_pos0 + min((t + 1) * group, n_q) - 1;
+  return q_pos0 + t;
+}
+
+template <int QF, int KF, int H, int D>
+__global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
+  constexpr bool F8MMA = (QF == FP8);          // fp8 x fp8 (keys are FP8 too)
+  constexpr int KB = (KF == FP8) ? 1 : 2;      // key bytes per element
+  constexpr int QB = (QF == FP8) ? 1 : 2;      // q bytes per element
+  constexpr int HALF = D / 2;                  // elements per lane half
+  constexpr int NL = HALF * KB / 16;           // 16-byte key loads per lane per step
+  constexpr int P = (16 / NL) > 8 ? 8 : (16 / NL);  // ring depth (steps in flight)
+  constexpr int KSTEP = F8MMA ? 32 : 8;        // elements per lane half per MFMA
+  constexpr int NKS = HALF / KSTEP;
+  constexpr int QW = 64 / H;                   // queries per wave
+  static_assert(P >= 2, "ring depth");
+  typedef typename std::conditional<F8MMA, i32x8, bf16x8>::type frag_t;
+
+  // LDS: [n_rows][kSplitBins] histograms, then the head weights of each
+  // wave's rows ([4 waves][2 halves][2 row blocks][16] floats; read by the
+  // epilogue instead of being held in registers)
+  extern __shared__ uint32_t shist[];
+  float* sw_all = (float*)(shist + a.n_rows * kSplitBins);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int l = lane_id(), half = l >> 5, l32 = l & 31;
+  const int b = blockIdx.y;
+  const int rwn = a.rwn, cwn = 4 / rwn;
+  const int rw = wave % rwn, cw = wave / rwn;
+
+  const int c_begin = (int)blockIdx.x * a.kc;
+  int c_end = min(c_begin + a.kc, a.n_k);
+  c_end = min(c_end, split_limit(a.mode, a.q_pos0, a.n_q, a.group, a.n_rows - 1) + 1);
+  if (c_begin >= c_end) {  // the whole workgroup: past every row's prefix
+    for (int t = threadIdx.x; t < a.n_rows; t += 256)
+      a.wbase[((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x] = -1;
+    return;
+  }
+
+  for (int i = threadIdx.x; i < a.n_rows * kSplitBins; i += 256) shist[i] = 0u;
+  __syncthreads();
+
+  // ---- resident q fragments and head weights of this wave's 64 rows ----
+  const int t_first = rw * QW;
+  frag_t afrag[2][NKS];
+  float* swv = sw_all + (wave * 2 + half) * 32;  // this lane's 32 weights
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int i = 32 * rb + l32;
+    const int t = t_first + i / H, h = i % H;
+    const bool ok = t < a.n_rows;
+    const char* rowp = (const char*)a.q +
+                       (((size_t)b * a.n_rows + (ok ? t : 0)) * H + h) * (size_t)D * QB + half * HALF * QB;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      frag_t f = *(const frag_t*)(rowp + ks * KSTEP * QB);
+      if (!ok) f = frag_t{};
+      afrag[rb][ks] = f;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ri = 32 * rb + 8 * (v / 4) + 4 * half + (v % 4);
+      const int tt = t_first + ri / H, hh = ri % H;
+      float wv = 0.f;
+      if (tt < a.n_rows) {
+        const size_t fr = (size_t)b * a.n_rows + tt;
+        wv = a.w[fr * H + hh];
+        if (QF == FP8) wv *= a.q_scale[fr];
+      }
+      if (l32 == 0) swv[rb * 16 + v] = wv;
+    }
+  }
+
+  // ---- this wave's 32-column steps: c_begin + 32 * (cw + cwn * i) ----
+  const int n_steps = (c_end - c_begin + 31) / 32;
+  const int n_my = cw < n_steps ? (n_steps - cw + cwn - 1) / cwn : 0;
+  const bool has_rows = t_first < a.n_rows;
+  const int n_run = has_rows ? n_my : 0;
+  const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * KB;
+  const float* kscl = (KF == FP8) ? a.k_scale + (size_t)b * a.n_k : nullptr;
+
+  i32x4 raw[P][NL];
+  float rsc[P];
+  // Loads are unconditional: a column past the chunk reads the chunk's last
+  // key row (in bounds) and is masked in the epilogue.
+  auto issue = [&](int s, int i) {  // s: ring slot (a constant after unrolling)
+    const int col = min(c_begin + 32 * (cw + cwn * i) + l32, c_end - 1);
+    const i32x4* src = (const i32x4*)(kseq + (size_t)col * D * KB + half * HALF * KB);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) raw[s][u] = src[u];
+    if constexpr (KF == FP8) rsc[s] = kscl[col];
+  };
+  auto bfrag = [&](const i32x4* r, int ks) -> frag_t {
+    if constexpr (F8MMA) {
+      const i32x4 x = r[2 * ks], y = r[2 * ks + 1];
+      return frag_t{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    } else if constexpr (KF == FP8) {
+      const i32x4 x = r[ks / 2];
+      uint32_t o0, o1, o2, o3;
+      fp8x4_to_bf16x4((uint32_t)x[(ks % 2) * 2], o0, o1);
+      fp8x4_to_bf16x4((uint32_t)x[(ks % 2) * 2 + 1], o2, o3);
+      return __builtin_bit_cast(frag_t, (i32x4{(int)o0, (int)o1, (int)o2, (int)o3}));
+    } else {
+      return __builtin_bit_cast(frag_t, r[ks]);
+    }
+  };
+  auto mma = [&](frag_t x, frag_t y, f32x16 c) -> f32x16 {
+    if constexpr (F8MMA)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+  };
+
+  // ---- epilogue of one step: ReLU, x w, head sum, key scale, mask, store, histogram ----
+  auto epilogue = [&](const f32x16* acc, int i, float ksc) {
+    const int col_raw = c_begin + 32 * (cw + cwn * i) + l32;
+    const int col = min(col_raw, c_end - 1);  // the column whose key this lane loaded
+    float wreg[2][16];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 x = ((const float4*)swv)[j];
+      wreg[j / 4][(j % 4) * 4 + 0] = x.x;
+      wreg[j / 4][(j % 4) * 4 + 1] = x.y;
+      wreg[j / 4][(j % 4) * 4 + 2] = x.z;
+      wreg[j / 4][(j % 4) * 4 + 3] = x.w;
+    }
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if ((32 * rb + 8 * (v / 4)) / H == qi) {
+            // ReLU as an integer max of the bits: negative floats (and -0)
+            // are negative integers, so they become +0 (one VALU op, no
+            // NaN canonicalisation; the MFMA results are finite)
+            const float r = __int_as_float(max(__float_as_int(acc[rb][v]), 0));
+            if (v & 1)
+              p1 = __builtin_fmaf(wreg[rb][v], r, p1);
+            else
+              p0 = __builtin_fmaf(wreg[rb][v], r, p0);
+          }
+      const float p = p0 + p1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+      const float tot = p + __uint_as_float(half ? sw[0] : sw[1]);
+      const int t = t_first + qi;
+      if constexpr (QW == 1) {
+        // Branch-free (keeps the step one scheduling region): every lane
+        // stores, since both halves hold the same total and a lane past the
+        // chunk computed the score of the chunk's last column, which it
+        // stores there again; only half 0's lanes inside the chunk count.
+        const bool ok = col <= split_limit(a.mode, a.q_pos0, a.n_q, a.group, t);
+        const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
+        a.out[((size_t)b * a.n_rows + t) * a.n_k + col] = val;
+        atomicAdd(&shist[t * kSplitBins + (order_key(val) >> kSplitShift)],
+                  (ok && half == 0 && col_raw < c_end) ? 1u : 0u);
+      } else {
+        // both halves hold the total; half (qi % 2) writes it
+        if (half == (qi & 1) && t < a.n_rows && col_raw < c_end) {
+          const bool ok = col <= split_limit(a.mode, a.q_pos0, a.n_q, a.group, t);
+          const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
+          a.out[((size_t)b * a.n_rows + t) * a.n_k + col] = val;
+          if (ok) atomicAdd(&shist[t * kSplitBins + (order_key(val) >> kSplitShift)], 1u);
+        }
+      }
+    }
+  };
+
+  // ---- ring-pipelined scan ----
+  // Step i: the MFMAs of step i (accumulator set i % 2) interleaved with the
+  // epilogue of step i - 1 (the other set), then the loads of step i + P into
+  // the ring slot step i just freed.  Every load is unconditional (clamped to
+  // the chunk, also past the last step) so that no ring register is
+  // conditionally live across the loop.
+  constexpr int NM = 2 * NKS;                 // MFMAs per step
+  constexpr int VPM = NM >= 16 ? 6 : 96 / NM;  // VALU ops placed after each
+  f32x16 acc[2][2];
+  float ksc[2] = {1.f, 1.f};
+  auto group = [&](auto first_c, int i0) {
+    constexpr bool FIRST = decltype(first_c)::value;
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+      const int i = i0 + s;
+      if (i < n_run) {
+        f32x16* c = acc[s & 1];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const frag_t bf = bfrag(raw[s], ks);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) c[rb] = mma(afrag[rb][ks], bf, ks == 0 ? f32x16{} : c[rb]);
+        }
+        if constexpr (KF == FP8) ksc[s & 1] = rsc[s];
+        issue(s, i + P);
+        if (!FIRST || s > 0) epilogue(acc[(s + 1) & 1], i - 1, ksc[(s + 1) & 1]);
+#pragma unroll
+        for (int j = 0; j < NM; ++j) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedVALU, VPM, 0);
+        }
+      }
+    }
+  };
+  if (n_run > 0) {
+#pragma unroll
+    for (int s = 0; s < P; ++s) issue(s, s);
+    group(std::true_type{}, 0);
+  }
+  for (int i0 = P; i0 < n_run; i0 += P) group(std::false_type{}, i0);
+  if (n_run > 0) {  // the last step (constant register indices on both branches)
+    if ((n_run - 1) & 1)
+      epilogue(acc[1], n_run - 1, ksc[1]);
+    else
+      epilogue(acc[0], n_run - 1, ksc[0]);
+  }
+
+  // ---- report each row's histogram window: the kSplitWin bins up to its top non-empty one ----
+  __syncthreads();
+  for (int t = wave; t < a.n_rows; t += 4) {
+    const uint32_t* hr = shist + t * kSplitBins;
+    int m = -1;
+#pragma unroll 16
+    for (int i = l; i < kSplitBins; i += kWave)
+      if (hr[i]) m = i;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+    const int wb = m < 0 ? -1 : max(m - kSplitWin + 1, 0);
+    const size_t slot = ((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x;
+    if (l == 0) a.wbase[slot] = wb;
+    for (int j = l; j < kSplitWin; j += kWave) a.win[slot * kSplitWin + j] = wb < 0 ? 0u : hr[wb + j];
+  }
+}
+
+// ---- compaction: threshold bin from the chunks' histogram windows, then
+// every score of this segment in or above it, in column order, into the
+// segment's slots of the candidate list ----
+//
+// A window covers the bins of its chunk from kSplitWin below the chunk's top
+// non-empty bin; counts below a window are dropped, so the summed histogram
+// can only undercount, the threshold bin only comes out lower, and the list
+// can only grow: it always holds the row's top-k.
+__global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
+  __shared__ uint32_t hist[kSplitBins];
+  __shared__ int wtot[4];
+  __shared__ int s_thr;
+  const int row = blockIdx.y;
+  const int t = row % a.n_rows;
+  const int len = min(split_limit(a.mode, a.q_pos0, a.n_q, a.group, t) + 1, a.n_k);
+  const int s0 = (int)blockIdx.x * a.seg, s1 = min(s0 + a.seg, len);
+  const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
+  int* segcnt = a.segcnt + (size_t)row * a.n_segs + blockIdx.x;
+  if (s0 >= s1) {
+    if (tid == 0) *segcnt = 0;
+    return;
+  }
+  const int need = min(a.topk, len);
+
+  for (int i = tid; i < kSplitBins; i += 256) hist[i] = 0u;
+  if (tid == 0) s_thr = 0;
+  __syncthreads();
+  const int* wb = a.wbase + (size_t)row * a.n_chunks;
+  const uint32_t* wn = a.win + (size_t)row * a.n_chunks * kSplitWin;
+  // batches of 8 windows' entries per thread: all loads in flight together
+  const int n_e = a.n_chunks * kSplitWin;
+  for (int e0 = 0; e0 < n_e; e0 += 8 * 256) {
+    uint32_t cv[8];
+    int bv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min(e0 + u * 256 + tid, n_e - 1);
+      bv[u] = wb[e / kSplitWin];
+      cv[u] = wn[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * 256 + tid;
+      if (e < n_e && bv[u] >= 0 && cv[u]) atomicAdd(&hist[bv[u] + e % kSplitWin], cv[u]);
+    }
+  }
+  __syncthreads();
+
+  // Block-wide exclusive prefix sum of one int per thread (+ the total).
+  auto block_scan = [&](int v, int* total) {
+    const int incl = wave_incl_scan(v);
+    if (l == kWave - 1) wtot[wave] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      before += w < wave ? wtot[w] : 0;
+      tot += wtot[w];
+    }
+    __syncthreads();
+    *total = tot;
+    return before + incl - v;
+  };
+
+  // thread i owns bins [16 i, 16 i + 16): the threshold is the highest bin
+  // with at least `need` counts at or above it (0 when the sum falls short)
+  uint32_t c[16];
+  int mine = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    c[j] = hist[16 * tid + j];
+    mine += (int)c[j];
+  }
+  int total;
+  const int before = block_scan(mine, &total);
+  int above = total - before - mine;  // counts in the bins of higher threads
+  if (above < need && above + mine >= need) {
+    for (int j = 15; j >= 0; --j) {
+      if (above + (int)c[j] >= need) {
+        s_thr = 16 * tid + j;
+        break;
+      }
+      above += (int)c[j];
+    }
+  }
+  __syncthreads();
+  const uint32_t thr = (uint32_t)s_thr;
+
+  const float* srow = a.scores + (size_t)row * a.n_k;
+  float* cv = a.cval + (size_t)row * a.n_k + s0;
+  int* ci = a.cidx + (size_t)row * a.n_k + s0;
+  int filled = 0;
+  for (int c0 = s0; c0 < s1; c0 += 16 * 256) {
+    float v[16];
+    uint32_t pm = 0;
+    int n = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int col = c0 + u * 256 + tid;
+      v[u] = srow[min(col, s1 - 1)];
+      const bool p = col < s1 && (order_key(v[u]) >> kSplitShift) >= thr;
+      pm |= (uint32_t)p << u;
+      n += p;
+    }
+    int tot;
+    int o = filled + block_scan(n, &tot);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if ((pm >> u) & 1u) {
+        cv[o] = v[u];
+        ci[o] = c0 + u * 256 + tid;
+        ++o;
+      }
+    }
+    filled += tot;
+  }
+  if (tid == 0) *segcnt = filled;
+}
+
+template <int QF, int KF, int H, int D>
+static hipError_t launch_split_t(const SplitArgs& a, int B, int chunks, hipStream_t st) {
+  const size_t lds = (size_t)a.n_rows * kSplitBins * 4 + 4 * 2 * 32 * 4;
+  hipLaunchKernelGGL((split_scan_kernel<QF, KF, H, D>), dim3(chunks, B), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int QF, int KF, int H>
+static hipError_t split_pick_d(const SplitArgs& a, int D, int B, int chunks, hipStream_t st) {
+  if (D == 64) return launch_split_t<QF, KF, H, 64>(a, B, chunks, st);
+  if (D == 128) return launch_split_t<QF, KF, H, 128>(a, B, chunks, st);
+  return hipErrorInvalidValue;
+}
+
+template <int QF, int KF>
+static hipError_t split_pick_h(const SplitArgs& a, int H, int D, int B, int chunks, hipStream_t st) {
+  if (H == 16) return split_pick_d<QF, KF, 16>(a, D, B, chunks, st);
+  if (H == 32) return split_pick_d<QF, KF, 32>(a, D, B, chunks, st);
+  if (H == 64) return split_pick_d<QF, KF, 64>(a, D, B, chunks, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_scan(const SplitArgs& a, int qf, int kf, int H, int D, int B, int chunks,
+                             hipStream_t st) {
+  if (qf == BF16 && kf == BF16) return split_pick_h<BF16, BF16>(a, H, D, B, chunks, st);
+  if (qf == BF16 && kf == FP8) return split_pick_h<BF16, FP8>(a, H, D, B, chunks, st);
+  if (qf == FP8 && kf == FP8) return split_pick_h<FP8, FP8>(a, H, D, B, chunks, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_compact(const CompactArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(split_compact_kernel, dim3(a.n_segs, rows), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace idx
