@@ -256,10 +256,25 @@ bool split_shape(const idx_problem* p, int n_rows, int qf) {
   return n_rows <= kSplitMaxRows && qf != IDX_F32 && p->k_dtype != IDX_F32;
 }
 
-// Key chunks of the split-key scan: about two workgroups per CU in one round.
-int split_kc(const idx_problem* p) {
-  const int chunks = std::max(1, std::min(ceil_div(512, p->batch), ceil_div(p->n_k, 128)));
-  return ceil_div(ceil_div(p->n_k, chunks), 128) * 128;
+// 64-row waves the rows of one sequence need in the split-key scan (1, 2 or 4).
+int split_rwn(const idx_problem* p, int n_rows) {
+  const int waves = ceil_div((long long)n_rows * p->heads, 64);
+  return waves <= 1 ? 1 : (waves <= 2 ? 2 : 4);
+}
+
+// Key columns per split-scan workgroup: a multiple of the column-group step,
+// aiming at one round of two workgroups per CU, else of one, else the
+// largest chunk the LDS holds.
+int split_kc(const idx_problem* p, int n_rows) {
+  const int rwn = split_rwn(p, n_rows), gran = 32 * (4 / rwn);
+  const int kb = p->k_dtype == IDX_FP8_E4M3 ? 1 : 2;
+  for (int per_cu = 2; per_cu >= 1; --per_cu) {
+    const int chunks = std::max(1, std::min(ceil_div(256 * per_cu, p->batch), ceil_div(p->n_k, gran)));
+    const int kc = ceil_div(ceil_div(p->n_k, chunks), gran) * gran;
+    if (split_lds_bytes(kb, p->dim, rwn, n_rows, kc) * per_cu <= kSplitLdsMax) return kc;
+  }
+  const size_t fixed = split_lds_bytes(kb, p->dim, rwn, n_rows, 0);
+  return std::max(gran, (int)((kSplitLdsMax - fixed) / (4 * (size_t)n_rows)) / gran * gran);
 }
 
 // Compaction segments: about 512 workgroups over all rows, at most kMaxSegs per row.
@@ -282,7 +297,7 @@ struct SplitLayout {
 SplitLayout split_layout(const idx_problem* p, int n_rows) {
   const size_t R = (size_t)p->batch * n_rows, row = (size_t)p->n_k * 4;
   SplitLayout s;
-  s.kc = split_kc(p);
+  s.kc = split_kc(p, n_rows);
   s.chunks = ceil_div(p->n_k, s.kc);
   s.seg = split_seg(p, n_rows);
   s.segs = ceil_div(p->n_k, s.seg);
@@ -321,8 +336,7 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   a.q_pos0 = p->q_pos0;
   a.group = group;
   a.mode = mode;
-  const int waves = ceil_div((long long)n_rows * p->heads, 64);
-  a.rwn = waves <= 1 ? 1 : (waves <= 2 ? 2 : 4);
+  a.rwn = split_rwn(p, n_rows);
   a.kc = sl.kc;
   a.out = scores;
   a.win = (uint32_t*)(region + sl.win);

@@ -80,6 +80,36 @@ constexpr int kSplitWin = 128;     // histogram bins a scan workgroup reports pe
 constexpr int kSplitMaxRows = 4;   // rows (queries or proxies) per sequence
 constexpr int kMaxSegs = 256;      // segments of a segmented list
 
+// Key-ring geometry of the split-key scan (shared by the kernel and the host
+// launcher, which sizes the LDS from it).  A step is 32 key columns; its
+// rows are fetched as 1 KiB direct-to-LDS copies, `rwn` row-waves sharing
+// them; the ring holds `split_ring_steps` steps per column group.
+constexpr int split_step_bytes(int key_bytes, int d) { return 32 * d * key_bytes; }
+constexpr int split_dma_waves(int key_bytes, int d, int rwn) {
+  return split_step_bytes(key_bytes, d) / 1024 < rwn ? split_step_bytes(key_bytes, d) / 1024 : rwn;
+}
+// VMEM operations one issuing wave has in flight per step: its share of the
+// key copies, plus the key-scale copy of FP8 keys
+constexpr int split_ops(int key_bytes, int d, int rwn) {
+  return split_step_bytes(key_bytes, d) / 1024 / split_dma_waves(key_bytes, d, rwn) + (key_bytes == 1 ? 1 : 0);
+}
+constexpr int split_ring_steps(int key_bytes, int d, int rwn) {
+  // about 40 KiB of ring (two workgroups fit a CU), at least 4 steps
+  const int by_lds0 = (40 * 1024) / ((4 / rwn) * split_step_bytes(key_bytes, d));
+  const int by_lds = by_lds0 < 4 ? 4 : by_lds0;
+  const int by_cnt = 2 + 63 / split_ops(key_bytes, d, rwn);                       // vmcnt holds 63
+  const int p = by_lds < by_cnt ? by_lds : by_cnt;
+  return p > 16 ? 16 : p;
+}
+// LDS bytes of a split-scan workgroup: ring, per-wave key-scale rings (FP8
+// keys), chunk scores, 16-bit-packed histograms, head weights.
+constexpr size_t split_lds_bytes(int key_bytes, int d, int rwn, int n_rows, int kc) {
+  return (size_t)(4 / rwn) * split_ring_steps(key_bytes, d, rwn) * split_step_bytes(key_bytes, d) +
+         (key_bytes == 1 ? (size_t)4 * split_ring_steps(key_bytes, d, rwn) * 256 : 0) +
+         (size_t)n_rows * kc * 4 + (size_t)n_rows * (kSplitBins / 2) * 4 + 4 * 2 * 32 * 4;
+}
+constexpr size_t kSplitLdsMax = 160 * 1024;
+
 struct SplitArgs {
   const void* q;          // [B, n_rows, H, D]
   const float* q_scale;   // [B, n_rows] (FP8 q only)
@@ -88,7 +118,7 @@ struct SplitArgs {
   const float* w;         // [B, n_rows, H]
   int n_rows, n_k, n_q, q_pos0, group, mode;  // mode: kModeDense or kModeProxy
   int rwn;                // 64-row waves per workgroup for the rows (1, 2 or 4)
-  int kc;                 // key columns per workgroup (grid.x = ceil(n_k / kc))
+  int kc;                 // key columns per workgroup (grid.x = ceil(n_k / kc)), a multiple of 32 * (4 / rwn)
   float* out;             // [B * n_rows, n_k] scores (-inf: masked)
   // per (row, chunk): the chunk's histogram bins [wbase, wbase + kSplitWin)
   // of that row, wbase = max(top non-empty bin - kSplitWin + 1, 0), or -1

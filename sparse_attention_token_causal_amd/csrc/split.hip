@@ -49,30 +49,67 @@ __device__ __forceinline__ int split_limit(int mode, int q_pos0, int n_q, int gr
   return q_pos0 + t;
 }
 
-template <int QF, int KF, int H, int D>
+// Waits until at most n vector-memory operations of this wave are in flight
+// (s_waitcnt with the export and LDS counters left at their maxima).
+#define IDX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+
+// LDS byte address of a pointer into workgroup memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land
+// at lds + BYTES * l (lds wave-uniform).  Written as inline assembly so that
+// the compiler does not pair every later LDS read with a wait for all
+// outstanding copies: the caller waits for them with s_waitcnt itself.  M0
+// (which holds the LDS base) is saved and restored; no VGPR is written.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
+  else
+    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
+}
+
+template <int QF, int KF, int H, int D, int RWN>
 __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
   constexpr bool F8MMA = (QF == FP8);          // fp8 x fp8 (keys are FP8 too)
   constexpr int KB = (KF == FP8) ? 1 : 2;      // key bytes per element
   constexpr int QB = (QF == FP8) ? 1 : 2;      // q bytes per element
   constexpr int HALF = D / 2;                  // elements per lane half
-  constexpr int NL = HALF * KB / 16;           // 16-byte key loads per lane per step
-  constexpr int P = (16 / NL) > 8 ? 8 : (16 / NL);  // ring depth (steps in flight)
+  constexpr int RB = D * KB;                   // key row bytes
+  constexpr int CK = RB / 16;                  // 16-byte chunks per key row
+  constexpr int NL = CK / 2;                   // chunks per lane half
+  constexpr int SB = split_step_bytes(KB, D);  // bytes per 32-column step
+  constexpr int NLD = SB / 1024;               // 1 KiB copies per step
+  constexpr int NLDI = split_dma_waves(KB, D, RWN);  // waves issuing them
+  constexpr int NLDW = NLD / NLDI;             // copies per issuing wave
+  constexpr int P = split_ring_steps(KB, D, RWN);
+  constexpr int OPS = split_ops(KB, D, RWN);   // VMEM ops per step, issuing wave
+  constexpr int OPS_REST = (KF == FP8) ? 1 : 0;  // ... other waves (scale copy only)
+  constexpr int CWN = 4 / RWN;                 // column groups
   constexpr int KSTEP = F8MMA ? 32 : 8;        // elements per lane half per MFMA
   constexpr int NKS = HALF / KSTEP;
   constexpr int QW = 64 / H;                   // queries per wave
-  static_assert(P >= 2, "ring depth");
+  static_assert(P >= 3, "ring depth");
   typedef typename std::conditional<F8MMA, i32x8, bf16x8>::type frag_t;
 
-  // LDS: [n_rows][kSplitBins] histograms, then the head weights of each
-  // wave's rows ([4 waves][2 halves][2 row blocks][16] floats; read by the
-  // epilogue instead of being held in registers)
-  extern __shared__ uint32_t shist[];
-  float* sw_all = (float*)(shist + a.n_rows * kSplitBins);
+  // LDS: key ring [CWN][P][SB] | key-scale rings [4 waves][P][64] (FP8) |
+  // chunk scores [n_rows][kc] | histograms [n_rows][kSplitBins / 2] (two
+  // 16-bit counters per word)
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* ring = smem;
+  float* sscale = (float*)(ring + CWN * P * SB);
+  float* ssc = sscale + ((KF == FP8) ? 4 * P * 64 : 0);
+  uint32_t* shist = (uint32_t*)(ssc + a.n_rows * a.kc);
+
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int l = lane_id(), half = l >> 5, l32 = l & 31;
   const int b = blockIdx.y;
-  const int rwn = a.rwn, cwn = 4 / rwn;
-  const int rw = wave % rwn, cw = wave / rwn;
+  const int rw = wave % RWN, cw = wave / RWN;
 
   const int c_begin = (int)blockIdx.x * a.kc;
   int c_end = min(c_begin + a.kc, a.n_k);
@@ -82,14 +119,14 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       a.wbase[((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x] = -1;
     return;
   }
-
-  for (int i = threadIdx.x; i < a.n_rows * kSplitBins; i += 256) shist[i] = 0u;
-  __syncthreads();
+  for (int i = threadIdx.x; i < a.n_rows * (kSplitBins / 2); i += 256) shist[i] = 0u;
 
   // ---- resident q fragments and head weights of this wave's 64 rows ----
+  // (lane half h holds the elements [h d/2, (h+1) d/2) of each row: the d
+  // axis is permuted the same way for the keys)
   const int t_first = rw * QW;
   frag_t afrag[2][NKS];
-  float* swv = sw_all + (wave * 2 + half) * 32;  // this lane's 32 weights
+  float wreg[2][16];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const int i = 32 * rb + l32;
@@ -103,38 +140,64 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       if (!ok) f = frag_t{};
       afrag[rb][ks] = f;
     }
+    // weights of the 16 result rows this lane holds (loads clamped to valid
+    // rows, all in flight together; rows past the set weigh 0)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int ri = 32 * rb + 8 * (v / 4) + 4 * half + (v % 4);
       const int tt = t_first + ri / H, hh = ri % H;
-      float wv = 0.f;
-      if (tt < a.n_rows) {
-        const size_t fr = (size_t)b * a.n_rows + tt;
-        wv = a.w[fr * H + hh];
-        if (QF == FP8) wv *= a.q_scale[fr];
-      }
-      if (l32 == 0) swv[rb * 16 + v] = wv;
+      const size_t fr = (size_t)b * a.n_rows + min(tt, a.n_rows - 1);
+      wreg[rb][v] = a.w[fr * H + hh] * (QF == FP8 ? a.q_scale[fr] : 1.f);
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int ri = 32 * rb + 8 * (v / 4) + 4 * half + (v % 4);
+      if (t_first + ri / H >= a.n_rows) wreg[rb][v] = 0.f;
     }
   }
+  __syncthreads();  // histograms zeroed, q loads done
 
-  // ---- this wave's 32-column steps: c_begin + 32 * (cw + cwn * i) ----
+  // ---- steps: group cw takes steps c_begin + 32 * (cw + CWN * i) ----
   const int n_steps = (c_end - c_begin + 31) / 32;
-  const int n_my = cw < n_steps ? (n_steps - cw + cwn - 1) / cwn : 0;
+  const int n_iter = (n_steps + CWN - 1) / CWN;  // the same for every wave (barriers)
+  const int n_my = cw < n_steps ? (n_steps - cw + CWN - 1) / CWN : 0;
   const bool has_rows = t_first < a.n_rows;
-  const int n_run = has_rows ? n_my : 0;
-  const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * KB;
+  const char* kseq = (const char*)a.k + (size_t)b * a.n_k * RB;
   const float* kscl = (KF == FP8) ? a.k_scale + (size_t)b * a.n_k : nullptr;
+  char* gring = ring + cw * P * SB;
+  float* wscale = sscale + wave * P * 64;
 
-  i32x4 raw[P][NL];
-  float rsc[P];
-  // Loads are unconditional: a column past the chunk reads the chunk's last
-  // key row (in bounds) and is masked in the epilogue.
-  auto issue = [&](int s, int i) {  // s: ring slot (a constant after unrolling)
-    const int col = min(c_begin + 32 * (cw + cwn * i) + l32, c_end - 1);
-    const i32x4* src = (const i32x4*)(kseq + (size_t)col * D * KB + half * HALF * KB);
+  // Direct-to-LDS copies of step i into ring slot i % P.  Copy dd of a step
+  // fills bytes [1024 dd, 1024 dd + 1024) of the slot, lane l the 16 bytes at
+  // 16 l: key r = p / CK, chunk position cp = p % CK (p = 64 dd + l), which
+  // holds the key's chunk cp ^ (r % CK) (an XOR swizzle: the 16-byte reads of
+  // 8 consecutive keys hit distinct bank groups).  Columns past the chunk
+  // copy its last key (in bounds; masked later).  Every wave also copies the
+  // 32 key scales of its own steps into its scale ring (FP8 keys).
+  auto issue = [&](int i) {
+    const int slot = i % P;
+    const int col0 = c_begin + 32 * (cw + CWN * i);
+    if (rw < NLDI) {
 #pragma unroll
-    for (int u = 0; u < NL; ++u) raw[s][u] = src[u];
-    if constexpr (KF == FP8) rsc[s] = kscl[col];
+      for (int d = 0; d < NLDW; ++d) {
+        const int dd = rw * NLDW + d;
+        const int p = dd * 64 + l;
+        const int r = p / CK, cp = p % CK;
+        const int key = min(col0 + r, c_end - 1);
+        copy_to_lds<16>(kseq + (size_t)key * RB + 16 * (cp ^ (r % CK)),
+                        __builtin_amdgcn_readfirstlane(lds_addr(gring + slot * SB + dd * 1024)));
+      }
+    }
+    if constexpr (KF == FP8) {
+      const int key = min(col0 + l32, c_end - 1);
+      copy_to_lds<4>(kscl + key, __builtin_amdgcn_readfirstlane(lds_addr(wscale + slot * 64)));
+    }
+  };
+  // this lane's half key row of step i: NL 16-byte chunks
+  auto read_keys = [&](int i, i32x4* raw) {
+    const char* row = gring + (i % P) * SB + l32 * RB;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) raw[u] = *(const i32x4*)(row + 16 * ((half * NL + u) ^ (l32 % CK)));
   };
   auto bfrag = [&](const i32x4* r, int ks) -> frag_t {
     if constexpr (F8MMA) {
@@ -157,19 +220,10 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
   };
 
-  // ---- epilogue of one step: ReLU, x w, head sum, key scale, mask, store, histogram ----
+  // ---- epilogue of step i: ReLU, x w, head sum, key scale, mask -> LDS scores + histogram ----
   auto epilogue = [&](const f32x16* acc, int i, float ksc) {
-    const int col_raw = c_begin + 32 * (cw + cwn * i) + l32;
-    const int col = min(col_raw, c_end - 1);  // the column whose key this lane loaded
-    float wreg[2][16];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float4 x = ((const float4*)swv)[j];
-      wreg[j / 4][(j % 4) * 4 + 0] = x.x;
-      wreg[j / 4][(j % 4) * 4 + 1] = x.y;
-      wreg[j / 4][(j % 4) * 4 + 2] = x.z;
-      wreg[j / 4][(j % 4) * 4 + 3] = x.w;
-    }
+    const int col_raw = c_begin + 32 * (cw + CWN * i) + l32;
+    const int col = min(col_raw, c_end - 1);  // the column whose key this lane used
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
       float p0 = 0.f, p1 = 0.f;
@@ -191,91 +245,121 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
       const float tot = p + __uint_as_float(half ? sw[0] : sw[1]);
       const int t = t_first + qi;
-      if constexpr (QW == 1) {
-        // Branch-free (keeps the step one scheduling region): every lane
-        // stores, since both halves hold the same total and a lane past the
-        // chunk computed the score of the chunk's last column, which it
-        // stores there again; only half 0's lanes inside the chunk count.
+      // Both halves hold the total; a lane past the chunk computed the score
+      // of the chunk's last column and stores it there again (same value).
+      // Only half (qi % 2)'s lanes inside the chunk count.
+      if (QW == 1 || t < a.n_rows) {
         const bool ok = col <= split_limit(a.mode, a.q_pos0, a.n_q, a.group, t);
         const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
-        a.out[((size_t)b * a.n_rows + t) * a.n_k + col] = val;
-        atomicAdd(&shist[t * kSplitBins + (order_key(val) >> kSplitShift)],
-                  (ok && half == 0 && col_raw < c_end) ? 1u : 0u);
-      } else {
-        // both halves hold the total; half (qi % 2) writes it
-        if (half == (qi & 1) && t < a.n_rows && col_raw < c_end) {
-          const bool ok = col <= split_limit(a.mode, a.q_pos0, a.n_q, a.group, t);
-          const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
-          a.out[((size_t)b * a.n_rows + t) * a.n_k + col] = val;
-          if (ok) atomicAdd(&shist[t * kSplitBins + (order_key(val) >> kSplitShift)], 1u);
-        }
+        ssc[t * a.kc + (col - c_begin)] = val;
+        const uint32_t bin = order_key(val) >> kSplitShift;
+        const bool count = ok && half == (qi & 1) && col_raw < c_end;
+        atomicAdd(&shist[t * (kSplitBins / 2) + (bin >> 1)], count ? (1u << (16 * (bin & 1))) : 0u);
       }
     }
   };
 
-  // ---- ring-pipelined scan ----
-  // Step i: the MFMAs of step i (accumulator set i % 2) interleaved with the
-  // epilogue of step i - 1 (the other set), then the loads of step i + P into
-  // the ring slot step i just freed.  Every load is unconditional (clamped to
-  // the chunk, also past the last step) so that no ring register is
-  // conditionally live across the loop.
+  // ---- pipelined scan ----
+  // Iteration i: wait for this wave's copies of step i + 1, barrier (every
+  // copy of step i + 1 has landed, every read of the slot refilled next is
+  // done), copy step i + P - 1 into the slot step i - 1 used, read step
+  // i + 1's keys from LDS into registers, then the MFMAs of step i
+  // (accumulator set i % 2) interleaved with the epilogue of step i - 1.
+  // The body is one basic block: a step past this group's end computes on
+  // its clamped keys (the chunk's last column, stored again with the same
+  // value and not counted), and a wave without rows computes nothing.  No
+  // global store is issued inside the loop, so the vector-memory counter
+  // only counts these copies (and they complete in order).
   constexpr int NM = 2 * NKS;                 // MFMAs per step
   constexpr int VPM = NM >= 16 ? 6 : 96 / NM;  // VALU ops placed after each
   f32x16 acc[2][2];
+  i32x4 raw[2][NL];
   float ksc[2] = {1.f, 1.f};
-  auto group = [&](auto first_c, int i0) {
+  auto wait_step = [&](auto after_c) {  // at most `after` steps of copies still in flight
+    constexpr int AFTER = decltype(after_c)::value;
+    if (rw < NLDI)
+      IDX_WAIT_VM(AFTER * OPS);
+    else
+      IDX_WAIT_VM(AFTER * OPS_REST);
+  };
+  auto iteration = [&](auto par_c, auto first_c, int i) {
+    constexpr int PAR = decltype(par_c)::value;  // i % 2
     constexpr bool FIRST = decltype(first_c)::value;
+    wait_step(std::integral_constant<int, P - 3>{});
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");  // no LDS access moves above the barrier
+    issue(i + P - 1);
+    if (has_rows) {
+      const float kprev = ksc[1 - PAR];  // step i - 1's scale; the slot takes step i + 1's
+      read_keys(i + 1, raw[1 - PAR]);
+      if constexpr (KF == FP8) ksc[1 - PAR] = wscale[((i + 1) % P) * 64 + l32];
+      f32x16* c = acc[PAR];
 #pragma unroll
-    for (int s = 0; s < P; ++s) {
-      const int i = i0 + s;
-      if (i < n_run) {
-        f32x16* c = acc[s & 1];
+      for (int ks = 0; ks < NKS; ++ks) {
+        const frag_t bf = bfrag(raw[PAR], ks);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const frag_t bf = bfrag(raw[s], ks);
+        for (int rb = 0; rb < 2; ++rb) c[rb] = mma(afrag[rb][ks], bf, ks == 0 ? f32x16{} : c[rb]);
+      }
+      if constexpr (!FIRST) epilogue(acc[1 - PAR], i - 1, kprev);
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) c[rb] = mma(afrag[rb][ks], bf, ks == 0 ? f32x16{} : c[rb]);
-        }
-        if constexpr (KF == FP8) ksc[s & 1] = rsc[s];
-        issue(s, i + P);
-        if (!FIRST || s > 0) epilogue(acc[(s + 1) & 1], i - 1, ksc[(s + 1) & 1]);
-#pragma unroll
-        for (int j = 0; j < NM; ++j) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedVALU, VPM, 0);
-        }
+      for (int j = 0; j < NM; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, VPM, 0);
       }
     }
   };
-  if (n_run > 0) {
-#pragma unroll
-    for (int s = 0; s < P; ++s) issue(s, s);
-    group(std::true_type{}, 0);
+  for (int i = 0; i < P - 1; ++i) issue(i);
+  wait_step(std::integral_constant<int, P - 2>{});  // step 0 landed
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+  if (has_rows) {
+    read_keys(0, raw[0]);
+    if constexpr (KF == FP8) ksc[0] = wscale[l32];
   }
-  for (int i0 = P; i0 < n_run; i0 += P) group(std::false_type{}, i0);
-  if (n_run > 0) {  // the last step (constant register indices on both branches)
-    if ((n_run - 1) & 1)
-      epilogue(acc[1], n_run - 1, ksc[1]);
+  iteration(std::integral_constant<int, 0>{}, std::true_type{}, 0);
+  int i = 1;
+  for (; i + 1 < n_iter; i += 2) {
+    iteration(std::integral_constant<int, 1>{}, std::false_type{}, i);
+    iteration(std::integral_constant<int, 0>{}, std::false_type{}, i + 1);
+  }
+  if (i < n_iter) iteration(std::integral_constant<int, 1>{}, std::false_type{}, i);
+  if (has_rows) {  // the last step's epilogue
+    if ((n_iter - 1) & 1)
+      epilogue(acc[1], n_iter - 1, ksc[1]);
     else
-      epilogue(acc[0], n_run - 1, ksc[0]);
+      epilogue(acc[0], n_iter - 1, ksc[0]);
+  }
+  IDX_WAIT_VM(0);   // the copies issued past the last step have landed too
+  __syncthreads();  // every score and count in LDS
+
+  // ---- chunk scores to global memory (coalesced) ----
+  const int width = c_end - c_begin;
+  for (int t = 0; t < a.n_rows; ++t) {
+    float* dst = a.out + ((size_t)b * a.n_rows + t) * a.n_k + c_begin;
+    for (int j = threadIdx.x; j < width; j += 256) dst[j] = ssc[t * a.kc + j];
   }
 
   // ---- report each row's histogram window: the kSplitWin bins up to its top non-empty one ----
-  __syncthreads();
   for (int t = wave; t < a.n_rows; t += 4) {
-    const uint32_t* hr = shist + t * kSplitBins;
+    const uint32_t* hr = shist + t * (kSplitBins / 2);
     int m = -1;
 #pragma unroll 16
-    for (int i = l; i < kSplitBins; i += kWave)
-      if (hr[i]) m = i;
+    for (int i = l; i < kSplitBins / 2; i += kWave) {
+      const uint32_t x = hr[i];
+      if (x) m = 2 * i + ((x >> 16) ? 1 : 0);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
     const int wb = m < 0 ? -1 : max(m - kSplitWin + 1, 0);
     const size_t slot = ((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x;
     if (l == 0) a.wbase[slot] = wb;
-    for (int j = l; j < kSplitWin; j += kWave) a.win[slot * kSplitWin + j] = wb < 0 ? 0u : hr[wb + j];
+    for (int j = l; j < kSplitWin; j += kWave) {
+      const int bin = wb + j;
+      a.win[slot * kSplitWin + j] = wb < 0 ? 0u : (hr[bin >> 1] >> (16 * (bin & 1))) & 0xFFFFu;
+    }
   }
 }
+#undef IDX_WAIT_VM
 
 // ---- compaction: threshold bin from the chunks' histogram windows, then
 // every score of this segment in or above it, in column order, into the
@@ -396,17 +480,37 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   if (tid == 0) *segcnt = filled;
 }
 
-template <int QF, int KF, int H, int D>
+template <int QF, int KF, int H, int D, int RWN>
 static hipError_t launch_split_t(const SplitArgs& a, int B, int chunks, hipStream_t st) {
-  const size_t lds = (size_t)a.n_rows * kSplitBins * 4 + 4 * 2 * 32 * 4;
-  hipLaunchKernelGGL((split_scan_kernel<QF, KF, H, D>), dim3(chunks, B), dim3(256), lds, st, a);
+  static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)split_scan_kernel<QF, KF, H, D, RWN>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSplitLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t lds = split_lds_bytes(KF == FP8 ? 1 : 2, D, RWN, a.n_rows, a.kc);
+  if (lds > kSplitLdsMax || a.kc % (32 * (4 / RWN)) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((split_scan_kernel<QF, KF, H, D, RWN>), dim3(chunks, B), dim3(256), lds, st, a);
   return hipGetLastError();
+}
+
+template <int QF, int KF, int H, int D>
+static hipError_t split_pick_rwn(const SplitArgs& a, int B, int chunks, hipStream_t st) {
+  if (a.rwn == 1) return launch_split_t<QF, KF, H, D, 1>(a, B, chunks, st);
+  if constexpr (H >= 32) {
+    if (a.rwn == 2) return launch_split_t<QF, KF, H, D, 2>(a, B, chunks, st);
+  }
+  if constexpr (H == 64) {
+    if (a.rwn == 4) return launch_split_t<QF, KF, H, D, 4>(a, B, chunks, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int QF, int KF, int H>
 static hipError_t split_pick_d(const SplitArgs& a, int D, int B, int chunks, hipStream_t st) {
-  if (D == 64) return launch_split_t<QF, KF, H, 64>(a, B, chunks, st);
-  if (D == 128) return launch_split_t<QF, KF, H, 128>(a, B, chunks, st);
+  if (D == 64) return split_pick_rwn<QF, KF, H, 64>(a, B, chunks, st);
+  if (D == 128) return split_pick_rwn<QF, KF, H, 128>(a, B, chunks, st);
   return hipErrorInvalidValue;
 }
 
