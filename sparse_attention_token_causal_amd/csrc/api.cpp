@@ -106,7 +106,8 @@ long long block_start_row(int mode, int blk, int total, int B, int n_rows, int n
 }
 
 struct Layout {
-  int mode, rw, BQ, total_blocks, n_rows, n_cols;
+  int mode, rw, nw, BQ, total_blocks, n_rows, n_cols;
+  bool filter;  // dense scan with candidate filtering (see ScoreArgs::filter)
 };
 
 Layout make_layout(int mode, const idx_problem* p, int n_rows, int n_cols, int group) {
@@ -121,9 +122,17 @@ Layout make_layout(int mode, const idx_problem* p, int n_rows, int n_cols, int g
     L.total_blocks = p->batch * ceil_div(p->n_q, group) * ceil_div(group, L.BQ);
   } else {
     L.rw = pick_rw(n_rows, p->heads);
+    L.nw = 8;
+    L.filter = false;
+    // Long dense scans with 64 heads (eight query-waves per workgroup, one
+    // query per wave) filter candidates
+    if (mode == kModeDense && p->heads == 64 && L.rw == 8) L.filter = true;
     L.BQ = queries_per_block(L.rw, p->heads);
     L.total_blocks = p->batch * ceil_div(n_rows, L.BQ);
+    return L;
   }
+  L.nw = 8;
+  L.filter = false;
   return L;
 }
 
@@ -153,7 +162,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
                      hipStream_t st, const Filter& flt = Filter()) {
   const int bpc = full ? L.total_blocks : (int)(buf_rows / L.BQ);
   if (bpc < 1) return IDX_EWORKSPACE;
-  const int tw = (8 / L.rw) * 64;
+  const int tw = (L.nw / L.rw) * 64;
   for (int blk0 = 0; blk0 < L.total_blocks; blk0 += bpc) {
     const int nb = (L.total_blocks - blk0 < bpc) ? L.total_blocks - blk0 : bpc;
     const long long r0 = block_start_row(L.mode, blk0, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
@@ -178,7 +187,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.ld = L.n_cols;
     sa.kc = kc;
     sa.rw = L.rw;
-    sa.nw = 8;
+    sa.nw = L.nw;
     sa.filter = flt.on ? 1 : 0;
     sa.cval = flt.val;
     sa.cidx = flt.idx;
@@ -232,9 +241,9 @@ ScoreArgs base_args(const idx_problem* p) {
   return a;
 }
 
-// Dense scans with 64 heads run eight query-waves per workgroup, one query
-// per wave: those filter candidates instead of writing full score rows.
-bool use_filter(const idx_problem* p, const Layout& L) { return p->heads == 64 && L.rw == 8; }
+// Long dense scans with 64 heads (one query per wave) filter candidates
+// instead of writing full score rows.
+bool use_filter(const idx_problem* p, const Layout& L) { return L.filter && p->heads == 64; }
 
 // Workspace bytes per buffered row of a dense scan: a float score row, or a
 // candidate list (float score + int key per slot) and its count.

@@ -315,18 +315,19 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   auto epilogue = [&](int cb, int c0, int key, float scale, bool live) {
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
-      float p0 = 0.f, p1 = 0.f;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent FMA chains
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           if ((32 * rb + 8 * (v / 4)) / H == qi) {
-            if (v & 1)
-              p1 = __builtin_fmaf(wreg[rb][v], fmaxf(acc[rb][cb][v], 0.f), p1);
-            else
-              p0 = __builtin_fmaf(wreg[rb][v], fmaxf(acc[rb][cb][v], 0.f), p0);
+            // ReLU as an integer max of the bits: negative floats (and -0)
+            // are negative integers, so they become +0 (one VALU op, no
+            // NaN canonicalisation; the MFMA results are finite)
+            const float r = __int_as_float(max(__float_as_int(acc[rb][cb][v]), 0));
+            ps[v & 3] = __builtin_fmaf(wreg[rb][v], r, ps[v & 3]);
           }
-      const float p = p0 + p1;
+      const float p = (ps[0] + ps[1]) + (ps[2] + ps[3]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
       const float other = __uint_as_float(cb == 0 ? sw[1] : sw[0]);
       const float tot = p + other;
