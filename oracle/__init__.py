@@ -15,11 +15,12 @@ from .formats import (bf16_bits_to_f64, e4m3fn_bits_to_f64, f64_to_bf16_bits_rne
 from .indexer import (causal_scores, dense_scores, select_topk, dense_topk, proxy_means,
                       round_proxy, proxy_limits, proxy_scores, proxy_candidates,
                       refine_topk, reuse_topk, grouped_reference, recall,
-                      group_bounds)
+                      group_bounds, block_means, block_limits, block_route, block_reference)
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "f64_to_bf16_bits_rne", "real_values",
     "causal_scores", "dense_scores", "select_topk", "dense_topk", "proxy_means", "round_proxy",
     "proxy_limits", "proxy_scores", "proxy_candidates", "refine_topk",
     "reuse_topk", "grouped_reference", "recall", "group_bounds",
+    "block_means", "block_limits", "block_route", "block_reference",
 ]

@@ -218,6 +218,70 @@ def grouped_reference(q, k, w, q_pos0, group, n_cand, topk, variant, q_fmt):
 
 
 # ----------------------------------------------------------------------------
+# block-mean routing (a second candidate generator for Refine)
+#
+# "AttentionIndex Architecture ...", "Why Positional Blocks Lose Recall" and
+# "Worked Example: Blocks Lose, Clusters Win": two-stage selection that routes
+# a query to contiguous blocks of keys ranked by a mean-pooled representative
+# of each block, keeps the best blocks, and runs the native indexer only on
+# the keys of the kept blocks.  Readings (the pages leave them open):
+#   * the router of a group is its PIVOT proxy, the block score is the native
+#     indexer form applied to the block mean;
+#   * a block is routable for a group only when all its keys lie in the
+#     prefix of the group's last member; the keys of the trailing partial
+#     block are always candidates;
+#   * the block mean is stored for the scan like the proxy (``round_proxy``).
+
+
+def block_means(k, block):
+    """kbar[j] = mean of the real keys of block j = [j*block, min((j+1)*block, n_k))."""
+    n_k = k.shape[0]
+    return np.stack([k[j : min(j + block, n_k)].mean(axis=0) for j in range(0, n_k, block)])
+
+
+def block_limits(n_q, group, q_pos0, block):
+    """Complete blocks in each group's prefix: floor((pos(t_last) + 1) / block)."""
+    return (proxy_limits(n_q, group, q_pos0) + 1) // block
+
+
+def block_route(qbar, wbar, kbar, k_lim, n_k, block, n_sel):
+    """Candidates of each group: the keys of its top min(n_sel, n_full) complete
+    blocks by (-B, j), B[g, j] = sum_h wbar relu(qbar_h . kbar_j), plus the
+    keys of the trailing partial block up to pos(t_last).
+
+    qbar, wbar: stored proxies; kbar: stored block means; k_lim: pos(t_last)
+    per group.  Returns (cand [n_g, (n_sel + 1) * block] ascending, -1 padded;
+    block scores [n_g, n_b] with -inf for blocks that are not routable; the
+    selected blocks [n_g, n_sel], -1 padded).
+    """
+    n_g, n_b = qbar.shape[0], kbar.shape[0]
+    width = (n_sel + 1) * block
+    n_full = (np.asarray(k_lim) + 1) // block
+    B = np.full((n_g, n_b), -np.inf)
+    rows, sel = [], []
+    for g in range(n_g):
+        f = int(n_full[g])
+        if f > 0:
+            B[g, :f] = np.maximum(kbar[:f] @ qbar[g].T, 0.0) @ wbar[g]
+        top = select_topk(B[g, :f], np.arange(f), n_sel)
+        sel.append(top)
+        keys = [np.arange(j * block, (j + 1) * block) for j in top]
+        keys.append(np.arange(f * block, int(k_lim[g]) + 1))
+        rows.append(np.sort(np.concatenate(keys)))
+    return _pad(rows, width), B, _pad(sel, n_sel)
+
+
+def block_reference(q, k, w, q_pos0, group, block, n_sel, topk, q_fmt, k_fmt):
+    """Block routing then Refine, entirely in the oracle, for one sequence."""
+    n_q = q.shape[0]
+    qbar, wbar = round_proxy(*proxy_means(q, w, group), q_fmt)
+    kbar, _ = round_proxy(block_means(k, block), np.zeros((1, 1)), k_fmt)
+    lim = proxy_limits(n_q, group, q_pos0)
+    cand, B, sel = block_route(qbar, wbar, kbar, lim, k.shape[0], block, n_sel)
+    return refine_topk(q, k, w, cand, group, q_pos0, topk), cand, B, sel
+
+
+# ----------------------------------------------------------------------------
 # measurement
 
 

@@ -434,6 +434,112 @@ def test_real_values_scale():
 
 
 # ----------------------------------------------------------------------------
+# block-mean routing ("AttentionIndex Architecture ...", "Why Positional Blocks
+# Lose Recall" and its worked example)
+
+
+def bf_block_route(q, k, w, q_pos0, G, S, n_sel, kk):
+    """Literal loops: proxy, block means, routable complete blocks, top blocks
+    by (-score, j), their keys plus the trailing partial block, then Refine."""
+    n_k = len(k)
+    out = [None] * len(q)
+    cands = []
+    for members in bf_groups(len(q), G):
+        qb, wb = bf_proxy(q, w, members)
+        lim = q_pos0 + members[-1]
+        n_full = (lim + 1) // S
+        pairs = []
+        for j in range(n_full):
+            rows = list(range(j * S, min(j * S + S, n_k)))
+            mean = [sum(k[s][c] for s in rows) / len(rows) for c in range(len(k[0]))]
+            pairs.append((bf_score([qb], [mean], [wb], 0, 0), j))
+        blocks = bf_select(pairs, n_sel)
+        cand = [s for j in blocks for s in range(j * S, j * S + S)] + list(range(n_full * S, lim + 1))
+        cands.append(sorted(cand))
+        for t in members:
+            v = [c for c in cand if c <= q_pos0 + t]
+            out[t] = bf_select([(bf_score(q, k, w, t, c), c) for c in v], kk)
+    return out, cands
+
+
+def block_case(q, k, w, q_pos0, G, S, n_sel, kk):
+    out, cand, _, _ = O.block_reference(q, k, w, q_pos0, G, S, n_sel, kk, "f32", "f32")
+    return as_sets(out), as_sets(cand)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_block_route(seed):
+    rng = np.random.default_rng(200 + seed)
+    n_q = int(rng.integers(1, 40))
+    n_k = n_q + int(rng.integers(0, 9))
+    H, d = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    q, k, w = tiny_int_case(rng, n_q, n_k, H, d)
+    # multiples of 12 make every proxy mean and every block mean (blocks of 1,
+    # 2, 3, 4; partial last blocks) exact in float32
+    q, k, w = q * 12.0, k * 12.0, w * 12.0
+    q_pos0 = n_k - n_q
+    for G in (1, 2, 4):
+        for S in (1, 2, 3, 4):
+            for n_sel in (1, 2, 5):
+                for kk in (1, 3):
+                    got = block_case(q, k, w, q_pos0, G, S, n_sel, kk)
+                    exp_out, exp_cand = bf_block_route(q.tolist(), k.tolist(), w.tolist(), q_pos0, G, S,
+                                                       n_sel, kk)
+                    assert got == (as_sets(exp_out), exp_cand)
+
+
+def test_block_size_one_is_the_proxy_scan():
+    """With one key per block every block is complete and its mean is the key:
+    the routed candidates are the proxy's top-n_sel."""
+    rng = np.random.default_rng(11)
+    q, k, w = tiny_int_case(rng, 24, 30, 2, 3)
+    q, w = q * 12.0, w * 12.0
+    for G, n_sel in ((1, 4), (3, 5), (8, 7)):
+        qb, wb = O.proxy_means(q, w, G)
+        lim = O.proxy_limits(24, G, 6)
+        ref = O.proxy_candidates(O.proxy_scores(qb, wb, k, lim), lim, n_sel)
+        cand, _, _ = O.block_route(qb, wb, O.block_means(k, 1), lim, 30, 1, n_sel)
+        assert as_sets(cand) == as_sets(ref)
+
+
+def test_all_blocks_kept_is_dense():
+    """Keeping every complete block (plus the partial tail) covers the whole
+    prefix, so Refine over it equals the dense top-k."""
+    rng = np.random.default_rng(12)
+    q, k, w = tiny_int_case(rng, 30, 30, 2, 3)
+    for S in (1, 4, 7):
+        out, cand, _, _ = O.block_reference(q, k, w, 0, 6, S, 30, 5, "f32", "f32")
+        assert as_sets(out) == as_sets(O.dense_topk(q, k, w, 0, 5))
+        for g, (a, b) in enumerate(O.group_bounds(30, 6)):
+            assert as_sets(cand[g : g + 1]) == [list(range(b))]
+
+
+def test_block_mean_hides_a_strong_key():
+    """The failure mode the pages describe: one high-scoring key in a block of
+    low ones ranks the block low on its mean, so routing to one block drops it."""
+    q = np.ones((1, 1, 1))
+    w = np.ones((1, 1))
+    k = np.array([[10.0], [-10.0], [-10.0], [-10.0], [1.0], [1.0], [1.0], [1.0]])
+    out, cand, B, sel = O.block_reference(q, k, w, 7, 1, 4, 1, 1, "f32", "f32")
+    assert B[0].tolist() == [0.0, 1.0]            # relu(-2.5) and relu(1.0)
+    assert sel[0].tolist() == [1]
+    assert as_sets(cand) == [[4, 5, 6, 7]]
+    assert as_sets(O.dense_topk(q, k, w, 7, 1)) == [[0]]
+    assert as_sets(out) == [[4]]
+
+
+def test_partial_block_is_not_routable():
+    """A block that reaches past the group's last member is not ranked (its mean
+    would include future keys); its visible keys are candidates anyway."""
+    q = np.ones((1, 1, 1))
+    w = np.ones((1, 1))
+    k = np.array([[1.0], [1.0], [1.0], [5.0], [100.0], [100.0]])  # the future keys are large
+    _, cand, B, sel = O.block_reference(q, k, w, 4, 1, 3, 1, 1, "f32", "f32")
+    assert np.isneginf(B[0, 1]) and sel[0].tolist() == [0]
+    assert as_sets(cand) == [[0, 1, 2, 3, 4]]
+
+
+# ----------------------------------------------------------------------------
 # mutation checks: each plausible mistake below is caught by a pin above
 
 
