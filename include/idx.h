@@ -76,7 +76,8 @@ enum {
   IDX_OP_SCORE_TOPK = 0,
   IDX_OP_GROUP_PROXY_SCAN = 1,
   IDX_OP_REFINE_TOPK = 2,
-  IDX_OP_REUSE_TOPK = 3
+  IDX_OP_REUSE_TOPK = 3,
+  IDX_OP_BLOCK_ROUTE = 4  /* n_cand = block size, topk = blocks kept */
 };
 
 /* One indexer problem: B sequences, each with n_q queries and n_k keys.
@@ -161,6 +162,34 @@ int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand
  *   proxy_topk [B, n_g, topk] int32, out_idx [B, n_q, topk] int32. */
 int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy_topk,
                        int32_t topk, int32_t* out_idx, void* stream);
+
+/* Block-mean candidate routing, a second candidate generator for
+ * idx_refine_topk ("AttentionIndex Architecture ...", "Why Positional Blocks
+ * Lose Recall" and "Worked Example: Blocks Lose, Clusters Win": contiguous
+ * blocks of keys are ranked by a mean-pooled representative, the best ones
+ * are kept, and the native indexer then runs only on their keys).
+ * Keys are cut into n_b = ceil(n_k / block) blocks of `block` consecutive
+ * positions (the last may be shorter); block j is represented by the mean of
+ * its real keys (float32 arithmetic, stored as bfloat16, or float32 for F32
+ * keys).  Group g (as in idx_group_proxy_scan) routes with its proxy: block
+ * j is routable iff all its keys lie in the prefix of the group's last
+ * member, n_full(g) = floor((pos(t_last) + 1) / block) of them; the group
+ * keeps the top min(n_sel, n_full(g)) routable blocks by
+ * sum_h wbar[h] * max(0, qbar[h,:] . mean_j), ties to the lower block index.
+ *   out_cand          [B, n_g, (n_sel + 1) * block] int32: the keys of the
+ *                     kept blocks, then the keys of the trailing partial
+ *                     block up to pos(t_last), padded with -1 (a candidate
+ *                     row for idx_refine_topk with n_cand = its width; the
+ *                     order within a row is unspecified).
+ *   out_block_means   optional [B, n_b, dim] (bfloat16 or float32).
+ *   out_block_scores  optional [B, n_g, n_b] float32, -inf where not routable.
+ *   out_proxy_q/_w    optional, as in idx_group_proxy_scan.
+ * ws: idx_workspace_bytes(p, IDX_OP_BLOCK_ROUTE, group, block, n_sel).
+ * IDX_EINVAL also for block < 1, n_sel < 1, or a row width beyond 2^31 - 1. */
+int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int32_t n_sel,
+                        int32_t* out_cand, void* out_block_means, float* out_block_scores,
+                        void* out_proxy_q, float* out_proxy_w, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /* Kernel timing (measurement aid, off by default).  While enabled, every
  * kernel the library enqueues is bracketed by a pair of HIP events recorded

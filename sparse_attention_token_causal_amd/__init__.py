@@ -22,7 +22,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsatc_idx.so")
 
 IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
-IDX_OP_SCORE_TOPK, IDX_OP_GROUP_PROXY_SCAN, IDX_OP_REFINE_TOPK, IDX_OP_REUSE_TOPK = 0, 1, 2, 3
+IDX_OP_SCORE_TOPK, IDX_OP_GROUP_PROXY_SCAN, IDX_OP_REFINE_TOPK, IDX_OP_REUSE_TOPK, IDX_OP_BLOCK_ROUTE = 0, 1, 2, 3, 4
 
 _DTYPES = {torch.float32: IDX_F32, torch.bfloat16: IDX_BF16, torch.float8_e4m3fn: IDX_FP8_E4M3}
 
@@ -73,6 +73,8 @@ def load_library():
         lib.idx_refine_topk.argtypes = [P, i32, vp, i32, i32, vp, vp, vp, sz, vp]
         lib.idx_reuse_topk.restype = i32
         lib.idx_reuse_topk.argtypes = [P, i32, vp, i32, vp, vp]
+        lib.idx_block_route.restype = i32
+        lib.idx_block_route.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.idx_profile_enable.restype = i32
         lib.idx_profile_enable.argtypes = [i32]
         lib.idx_profile_read.restype = i32
@@ -224,6 +226,44 @@ def reuse_topk(proxy_topk, group, n_q, n_k, q_pos0=None, out=None):
     return idx
 
 
+def block_route(q, k, w, group, block, n_sel, q_scale=None, k_scale=None, q_pos0=None,
+                return_means=False, return_scores=False, return_proxy=False, workspace=None):
+    """Block-mean routing: candidates int32 [B, n_g, (n_sel + 1) * block] (-1 padded).
+
+    ``return_means`` adds the stored block means [B, n_b, d] (bfloat16, or
+    float32 for float32 keys); ``return_scores`` adds the block scores
+    [B, n_g, n_b] (-inf where a block is not routable); ``return_proxy`` adds
+    the stored proxy q and w.
+    """
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    B, n_q, H, d = q.shape
+    n_k = k.shape[1]
+    n_g, n_b = -(-n_q // group), -(-n_k // block)
+    cand = torch.empty((B, n_g, (n_sel + 1) * block), dtype=torch.int32, device=q.device)
+    km = bs = pq = pw = None
+    if return_means:
+        km = torch.empty((B, n_b, d), dtype=torch.float32 if k.dtype == torch.float32 else torch.bfloat16,
+                         device=q.device)
+    if return_scores:
+        bs = torch.empty((B, n_g, n_b), dtype=torch.float32, device=q.device)
+    if return_proxy:
+        pq = torch.empty((B, n_g, H, d), dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
+                         device=q.device)
+        pw = torch.empty((B, n_g, H), dtype=torch.float32, device=q.device)
+    ws = _workspace(p, IDX_OP_BLOCK_ROUTE, q.device, group, block, n_sel, workspace=workspace)
+    _check(lib.idx_block_route(ctypes.byref(p), group, block, n_sel, _ptr(cand), _ptr(km), _ptr(bs), _ptr(pq),
+                               _ptr(pw), _ptr(ws), ws.numel(), _stream(q.device)))
+    res = [cand]
+    if return_means:
+        res.append(km)
+    if return_scores:
+        res.append(bs)
+    if return_proxy:
+        res += [pq, pw]
+    return res[0] if len(res) == 1 else tuple(res)
+
+
 KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill")
 
 
@@ -241,5 +281,6 @@ def profile_read():
     return {KERNEL_KINDS[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
 
 
-__all__ = ["profile_enable", "profile_read", "score_topk", "group_proxy_scan", "refine_topk", "reuse_topk", "make_problem",
+__all__ = ["profile_enable", "profile_read", "score_topk", "group_proxy_scan", "refine_topk", "reuse_topk",
+           "block_route", "make_problem",
            "workspace_bytes", "load_library", "library_path", "IndexerError"]

@@ -206,6 +206,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     se.q_pos0 = sa.q_pos0;
     se.n_q = n_q;
     se.group = group;
+    se.block = sa.block;
     se.cand = sa.cand;
     se.lidx = nullptr;
     se.counts = nullptr;
@@ -235,6 +236,7 @@ ScoreArgs base_args(const idx_problem* p) {
   a.n_q = p->n_q;
   a.q_pos0 = p->q_pos0;
   a.group = 1;
+  a.block = 1;
   a.n_cols = p->n_k;
   a.cand = nullptr;
   a.mode = kModeDense;
@@ -328,8 +330,8 @@ SplitLayout split_layout(const idx_problem* p, int n_rows) {
 // (already filled with -inf by the caller); otherwise the region's own
 // buffer holds them.
 int split_score_select(const idx_problem* p, int qf, const void* q, const float* q_scale,
-                       const float* w, int n_rows, int mode, int group, int topk, int* out,
-                       float* scores, char* region, hipStream_t st) {
+                       const float* w, int n_rows, int mode, int group, int block, int topk,
+                       int* out, float* scores, char* region, hipStream_t st) {
   const SplitLayout sl = split_layout(p, n_rows);
   const int B = p->batch, R = B * n_rows;
   if (!scores) scores = (float*)(region + sl.scores);
@@ -345,6 +347,7 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   a.q_pos0 = p->q_pos0;
   a.group = group;
   a.mode = mode;
+  a.block = block;
   a.rwn = split_rwn(p, n_rows);
   a.kc = sl.kc;
   a.out = scores;
@@ -366,6 +369,7 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   c.q_pos0 = p->q_pos0;
   c.group = group;
   c.mode = mode;
+  c.block = block;
   c.topk = topk;
   c.seg = sl.seg;
   c.n_segs = sl.segs;
@@ -382,6 +386,7 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   se.q_pos0 = p->q_pos0;
   se.n_q = p->n_q;
   se.group = group;
+  se.block = block;
   se.lidx = c.cidx;
   se.seg_counts = c.segcnt;
   se.n_segs = sl.segs;
@@ -398,6 +403,55 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
       }) != hipSuccess)
     return IDX_EHIP;
   return IDX_OK;
+}
+
+
+// Block routing: the block-mean "keys" the proxy scans (bfloat16, float32
+// for float32 keys) and the problem that scan is: the group proxies against
+// n_b = ceil(n_k / block) block means, positions unchanged.
+int block_mean_dtype(const idx_problem* p) { return p->k_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
+
+idx_problem block_problem(const idx_problem* p, int block, const void* pq, const float* pw,
+                          const void* kbar) {
+  idx_problem q = *p;
+  q.n_k = ceil_div(p->n_k, block);
+  q.q_dtype = proxy_q_dtype(p);
+  q.k_dtype = block_mean_dtype(p);
+  q.q = pq;
+  q.q_scale = nullptr;
+  q.k = kbar;
+  q.k_scale = nullptr;
+  q.w = pw;
+  return q;
+}
+
+struct BlockLayout {
+  size_t pq, pw, kbar, sel, scan, total;  // byte offsets
+  bool split;
+  long long rows;  // score rows the tiled scan's buffer holds
+};
+
+BlockLayout block_layout(const idx_problem* p, int group, int block, int n_sel) {
+  const int n_g = ceil_div(p->n_q, group);
+  const idx_problem q = block_problem(p, block, nullptr, nullptr, nullptr);
+  BlockLayout L;
+  size_t o = 0;
+  L.pq = o;   o += align_up(proxy_q_bytes(p, n_g));
+  L.pw = o;   o += align_up((size_t)p->batch * n_g * p->heads * 4);
+  L.kbar = o; o += align_up((size_t)p->batch * q.n_k * p->dim * (q.k_dtype == IDX_F32 ? 4 : 2));
+  L.sel = o;  o += align_up((size_t)p->batch * n_g * n_sel * 4);
+  L.scan = o;
+  L.split = split_shape(&q, n_g, q.q_dtype);
+  if (L.split) {
+    L.rows = 0;
+    o += split_layout(&q, n_g).total;
+  } else {
+    Layout S = make_layout(kModeBlock, &q, n_g, q.n_k, group);
+    L.rows = buffer_rows(S, (long long)p->batch * n_g);
+    o += align_up((size_t)L.rows * q.n_k * 4);
+  }
+  L.total = o;
+  return L;
 }
 
 }  // namespace
@@ -435,6 +489,10 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
     Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
     return proxy + align_up((size_t)buffer_rows(L, (long long)p->batch * n_g) * p->n_k * 4);
   }
+  if (op == IDX_OP_BLOCK_ROUTE) {  // n_cand = block size, topk = blocks kept
+    if (n_cand < 1 || topk < 1) return 0;
+    return block_layout(p, group, n_cand, topk).total;
+  }
   if (op == IDX_OP_REFINE_TOPK) {
     if (n_cand < 1) return 0;
     Layout L = make_layout(kModeGather, p, p->n_q, n_cand, group);
@@ -457,7 +515,7 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
           return launch_fill(out_scores, (size_t)p->batch * p->n_q * p->n_k, -__builtin_huge_valf(), st);
         }) != hipSuccess)
       return IDX_EHIP;
-    return split_score_select(p, p->q_dtype, p->q, p->q_scale, p->w, p->n_q, kModeDense, 1, topk,
+    return split_score_select(p, p->q_dtype, p->q, p->q_scale, p->w, p->n_q, kModeDense, 1, 1, topk,
                               out_idx, out_scores, (char*)ws, st);
   }
   Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
@@ -519,7 +577,7 @@ int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand
           return launch_fill(out_proxy_scores, (size_t)p->batch * n_g * p->n_k, -__builtin_huge_valf(), st);
         }) != hipSuccess)
       return IDX_EHIP;
-    return split_score_select(p, pqf, pq, nullptr, pw, n_g, kModeProxy, group, n_cand, out_cand,
+    return split_score_select(p, pqf, pq, nullptr, pw, n_g, kModeProxy, group, 1, n_cand, out_cand,
                               out_proxy_scores, cur, st);
   }
   Layout L = make_layout(kModeProxy, p, n_g, p->n_k, group);
@@ -584,6 +642,60 @@ int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy
   hipStream_t st = (hipStream_t)stream;
   if (timed(IDX_KERNEL_REUSE, st, [&] {
         return launch_reuse(proxy_topk, p->batch, p->n_q, p->q_pos0, group, topk, out_idx, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  return IDX_OK;
+}
+
+int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int32_t n_sel,
+                        int32_t* out_cand, void* out_block_means, float* out_block_scores,
+                        void* out_proxy_q, float* out_proxy_w, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  if (group < 1 || block < 1 || n_sel < 1 || !out_cand) return IDX_EINVAL;
+  if ((long long)(n_sel + 1) * block > 0x7FFFFFFF) return IDX_EINVAL;
+  const BlockLayout BL = block_layout(p, group, block, n_sel);
+  if (!ws || ws_bytes < BL.total) return IDX_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const int n_g = ceil_div(p->n_q, group);
+  char* base = (char*)ws;
+  void* pq = out_proxy_q ? out_proxy_q : (void*)(base + BL.pq);
+  float* pw = out_proxy_w ? out_proxy_w : (float*)(base + BL.pw);
+  void* kbar = out_block_means ? out_block_means : (void*)(base + BL.kbar);
+  int* sel = (int*)(base + BL.sel);
+  if (timed(IDX_KERNEL_PROXY, st, [&] {
+        hipError_t e = launch_proxy_build(p->q, p->q_scale, p->w, p->batch, p->n_q, p->heads, p->dim,
+                                          p->q_dtype, group, pq, pw, st);
+        return e != hipSuccess ? e
+                               : launch_block_means(p->k, p->k_scale, p->batch, p->n_k, p->dim, p->k_dtype,
+                                                    block, kbar, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  const idx_problem q = block_problem(p, block, pq, pw, kbar);
+  const bool full = out_block_scores != nullptr;
+  if (full && timed(IDX_KERNEL_FILL, st, [&] {
+        return launch_fill(out_block_scores, (size_t)p->batch * n_g * q.n_k, -__builtin_huge_valf(), st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  if (BL.split) {
+    rc = split_score_select(&q, q.q_dtype, pq, nullptr, pw, n_g, kModeBlock, group, block, n_sel, sel,
+                            out_block_scores, base + BL.scan, st);
+  } else {
+    Layout L = make_layout(kModeBlock, &q, n_g, q.n_k, group);
+    ScoreArgs sa = base_args(&q);
+    sa.n_rows = n_g;
+    sa.group = group;
+    sa.block = block;
+    sa.mode = kModeBlock;
+    float* buf = full ? out_block_scores : (float*)(base + BL.scan);
+    const long long rows = full ? (long long)p->batch * n_g : BL.rows;
+    rc = score_and_select(sa, L, q.q_dtype, q.k_dtype, p->heads, p->dim, p->batch, p->n_q, group, buf,
+                          rows, full, n_sel, sel, st);
+  }
+  if (rc != IDX_OK) return rc;
+  if (timed(IDX_KERNEL_REUSE, st, [&] {
+        return launch_block_expand(sel, p->batch, p->n_q, p->q_pos0, group, block, n_sel, out_cand, st);
       }) != hipSuccess)
     return IDX_EHIP;
   return IDX_OK;

@@ -15,6 +15,18 @@ constexpr int kModeDense = 0;   // rows = queries, columns = key positions, row 
 constexpr int kModeProxy = 1;   // rows = group proxies, row limit = last member's position
 constexpr int kModeGather = 2;  // rows = queries, columns = the group's candidate list
 constexpr int kModeList = 3;    // select only: rows are candidate lists (score, key index)
+constexpr int kModeBlock = 4;   // rows = group proxies, columns = key blocks (block means)
+
+// Last visible column of row r (-1: none).  Dense: the query's position;
+// proxy: the position of the group's last member; block: the last key block
+// lying wholly inside that member's prefix (blocks of `block` keys).
+__host__ __device__ inline int mode_limit(int mode, int q_pos0, int n_q, int group, int block, int r) {
+  if (mode == kModeProxy || mode == kModeBlock) {
+    const int last = q_pos0 + ((r + 1) * group < n_q ? (r + 1) * group : n_q) - 1;
+    return mode == kModeProxy ? last : (last + 1) / block - 1;
+  }
+  return q_pos0 + r;
+}
 
 struct ScoreArgs {
   const void* q;          // [B, n_rows, H, D] rows (queries or proxies)
@@ -23,6 +35,7 @@ struct ScoreArgs {
   const float* k_scale;   // [B, n_k] (FP8 k only)
   const float* w;         // [B, n_rows, H]
   int n_rows, n_k, n_q, q_pos0, group;
+  int block;              // key-block size (kModeBlock)
   int n_cols;             // n_k (dense, proxy) or n_cand (gather)
   const int* cand;        // [B, n_g, n_cand] (gather only)
   int mode;
@@ -54,7 +67,7 @@ struct SelectArgs {
   int n_cols;
   int mode;               // kModeDense / kModeProxy: length = limit + 1; kModeGather: all n_cols, -inf = excluded;
                           // kModeList: length = counts[i], key index = lidx[i * ld + c]
-  int q_pos0, n_q, group;
+  int q_pos0, n_q, group, block;
   const int* cand;        // gather: key index of each column
   const int* lidx;        // list: key indices, same layout as scores
   const int* counts;      // list: entries per launch row
@@ -116,7 +129,8 @@ struct SplitArgs {
   const void* k;          // [B, n_k, D]
   const float* k_scale;   // [B, n_k] (FP8 k only)
   const float* w;         // [B, n_rows, H]
-  int n_rows, n_k, n_q, q_pos0, group, mode;  // mode: kModeDense or kModeProxy
+  int n_rows, n_k, n_q, q_pos0, group, mode;  // mode: kModeDense, kModeProxy or kModeBlock
+  int block;              // key-block size (kModeBlock)
   int rwn;                // 64-row waves per workgroup for the rows (1, 2 or 4)
   int kc;                 // key columns per workgroup (grid.x = ceil(n_k / kc)), a multiple of 32 * (4 / rwn)
   float* out;             // [B * n_rows, n_k] scores (-inf: masked)
@@ -134,6 +148,7 @@ struct CompactArgs {
   const int* wbase;
   int n_chunks;
   int n_rows, n_k, n_q, q_pos0, group, mode, topk;
+  int block;              // key-block size (kModeBlock)
   int seg;                // columns per workgroup (grid.x = n_segs = ceil(n_k / seg))
   int n_segs;
   float* cval;            // [B * n_rows, n_k]: segment s's candidates from s * seg
@@ -152,5 +167,9 @@ hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* 
                               hipStream_t st);
 hipError_t launch_reuse(const int* ptop, int B, int n_q, int q_pos0, int group, int topk,
                         int* out, hipStream_t st);
+hipError_t launch_block_means(const void* k, const float* k_scale, int B, int n_k, int D, int kf,
+                              int block, void* kbar, hipStream_t st);
+hipError_t launch_block_expand(const int* sel, int B, int n_q, int q_pos0, int group, int block,
+                               int n_sel, int* cand, hipStream_t st);
 
 }  // namespace idx

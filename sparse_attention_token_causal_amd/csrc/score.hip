@@ -95,8 +95,7 @@ struct MfmaTraits<FP8, FP8> {
 };
 
 __device__ __forceinline__ int row_limit(const ScoreArgs& a, int r) {
-  if (a.mode == kModeProxy) return a.q_pos0 + min((r + 1) * a.group, a.n_q) - 1;
-  return a.q_pos0 + r;
+  return mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, r);
 }
 
 // Scheduling groups for the instruction scheduler (gfx9 sched_group_barrier masks).

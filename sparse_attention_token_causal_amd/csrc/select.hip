@@ -52,8 +52,7 @@ struct SelectShared {
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
   if (a.mode == kModeList) return min(a.counts[blockIdx.x], a.n_cols);
   if (a.mode == kModeGather) return a.n_cols;
-  const int lim = (a.mode == kModeProxy) ? a.q_pos0 + min((r + 1) * a.group, a.n_q) - 1
-                                         : a.q_pos0 + r;
+  const int lim = mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, r);
   return min(lim + 1, a.n_cols);
 }
 
@@ -462,8 +461,7 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
     auto len_of = [&](long long i) {
       const long long fr = a.row0 + i;
       const int rr = (int)(fr % a.n_rows);
-      const int lim = (a.mode == kModeProxy) ? a.q_pos0 + std::min((rr + 1) * a.group, a.n_q) - 1
-                                             : a.q_pos0 + rr;
+      const int lim = mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, rr);
       return std::min(lim + 1, a.n_cols);
     };
     int cls = 4;

@@ -44,11 +44,6 @@ constexpr int kSplitShift = 32 - 12;  // histogram bin = order key >> kSplitShif
 // gfx9 sched_group_barrier instruction classes
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
 
-__device__ __forceinline__ int split_limit(int mode, int q_pos0, int n_q, int group, int t) {
-  if (mode == kModeProxy) return q_pos0 + min((t + 1) * group, n_q) - 1;
-  return q_pos0 + t;
-}
-
 // Waits until at most n vector-memory operations of this wave are in flight
 // (s_waitcnt with the export and LDS counters left at their maxima).
 #define IDX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
@@ -113,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
 
   const int c_begin = (int)blockIdx.x * a.kc;
   int c_end = min(c_begin + a.kc, a.n_k);
-  c_end = min(c_end, split_limit(a.mode, a.q_pos0, a.n_q, a.group, a.n_rows - 1) + 1);
+  c_end = min(c_end, mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, a.n_rows - 1) + 1);
   if (c_begin >= c_end) {  // the whole workgroup: past every row's prefix
     for (int t = threadIdx.x; t < a.n_rows; t += 256)
       a.wbase[((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x] = -1;
@@ -249,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       // of the chunk's last column and stores it there again (same value).
       // Only half (qi % 2)'s lanes inside the chunk count.
       if (QW == 1 || t < a.n_rows) {
-        const bool ok = col <= split_limit(a.mode, a.q_pos0, a.n_q, a.group, t);
+        const bool ok = col <= mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, t);
         const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
         ssc[t * a.kc + (col - c_begin)] = val;
         const uint32_t bin = order_key(val) >> kSplitShift;
@@ -375,7 +370,7 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   __shared__ int s_thr;
   const int row = blockIdx.y;
   const int t = row % a.n_rows;
-  const int len = min(split_limit(a.mode, a.q_pos0, a.n_q, a.group, t) + 1, a.n_k);
+  const int len = min(mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, t) + 1, a.n_k);
   const int s0 = (int)blockIdx.x * a.seg, s1 = min(s0 + a.seg, len);
   const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
   int* segcnt = a.segcnt + (size_t)row * a.n_segs + blockIdx.x;

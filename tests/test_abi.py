@@ -27,7 +27,7 @@ def lib():
 def test_header_declares_the_four_entry_points():
     fns = declared_functions()
     for f in ("idx_score_topk", "idx_group_proxy_scan", "idx_refine_topk", "idx_reuse_topk",
-              "idx_workspace_bytes", "idx_status_string", "idx_version"):
+              "idx_block_route", "idx_workspace_bytes", "idx_status_string", "idx_version"):
         assert f in fns
 
 
@@ -84,6 +84,15 @@ def test_invalid_call_arguments(lib):
     assert lib.idx_reuse_topk(ctypes.byref(p), 0, FAKE, 8, FAKE, None) == -1
     assert lib.idx_reuse_topk(ctypes.byref(p), 4, None, 8, FAKE, None) == -1
     assert lib.idx_reuse_topk(ctypes.byref(problem(n_q=65)), 4, FAKE, 8, FAKE, None) == -1
+    # block routing: group, block, blocks kept, output, row width
+    assert lib.idx_block_route(ctypes.byref(p), 0, 8, 2, FAKE, None, None, None, None, None, 0, None) == -1
+    assert lib.idx_block_route(ctypes.byref(p), 4, 0, 2, FAKE, None, None, None, None, None, 0, None) == -1
+    assert lib.idx_block_route(ctypes.byref(p), 4, 8, 0, FAKE, None, None, None, None, None, 0, None) == -1
+    assert lib.idx_block_route(ctypes.byref(p), 4, 8, 2, None, None, None, None, None, None, 0, None) == -1
+    assert lib.idx_block_route(ctypes.byref(p), 4, 1 << 20, 1 << 12, FAKE, None, None, None, None, None, 0,
+                               None) == -1
+    assert lib.idx_block_route(ctypes.byref(problem(q=None)), 4, 8, 2, FAKE, None, None, None, None, None, 0,
+                               None) == -1
 
 
 def test_workspace_checks(lib):
@@ -98,6 +107,10 @@ def test_workspace_checks(lib):
     need_r = lib.idx_workspace_bytes(ctypes.byref(p), 2, 4, 16, 8)
     assert lib.idx_refine_topk(ctypes.byref(p), 4, FAKE, 16, 8, FAKE, None, FAKE, need_r - 1, None) == -3
     assert lib.idx_workspace_bytes(ctypes.byref(p), 3, 4, 16, 8) == 0
+    need_b = lib.idx_workspace_bytes(ctypes.byref(p), 4, 4, 8, 2)
+    assert need_b > 0
+    assert lib.idx_block_route(ctypes.byref(p), 4, 8, 2, FAKE, None, None, None, None, FAKE, need_b - 1,
+                               None) == -3
 
 
 def test_workspace_sizes_follow_the_layout(lib):
@@ -117,3 +130,7 @@ def test_workspace_sizes_follow_the_layout(lib):
     # proxy scan: proxy q (bf16) + proxy w + score rows
     g = lib.idx_workspace_bytes(ctypes.byref(p), 1, 10, 64, 0)
     assert g >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + 100 * 1000 * 4
+    # block routing: proxy q + w, block means (bf16), kept blocks, block-score rows
+    br = lib.idx_workspace_bytes(ctypes.byref(p), 4, 10, 16, 3)
+    n_b = -(-1000 // 16)
+    assert br >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + n_b * 128 * 2 + 100 * 3 * 4 + 100 * n_b * 4

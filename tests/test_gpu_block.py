@@ -1,0 +1,108 @@
+"""GPU vs oracle parity of block-mean candidate routing (through the C ABI).
+
+Chain, as for the proxy scan: the stored proxy and block means are the
+rounded means; the block scores on the GPU's own proxy and means match the
+oracle within the score tolerance; the routed candidates equal the oracle's
+routing on the GPU's own block scores (exact, as sets); Refine over them is
+valid and, with every block kept, equals the dense path.  Shapes cover the
+tiled scan (many groups) and the split-key scan (at most four groups per
+sequence), FP8 and float32 keys, blocks of 1 and ragged last blocks.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_token_causal_amd as S
+from sparse_attention_token_causal_amd.synth import Workload, make_inputs
+
+from parity import assert_same_sets, check_rows_valid, check_scores, cuda, real_inputs, sets
+
+pytestmark = pytest.mark.gpu
+
+# (workload, block, blocks kept)
+CASES = [
+    (Workload("blk_bf16_L1000_G16", 1, 1000, 1000, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98,
+              topk=64, group=16, seed=31), 32, 6),
+    (Workload("blk_fp8_L777_G64", 1, 777, 777, 64, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99,
+              topk=40, group=64, seed=32), 48, 4),
+    (Workload("blk_f32_B2_L300_H16_d64_G5", 2, 300, 300, 16, 64, "f32", "f32", "normal8", "normal8",
+              topk=11, group=5, seed=33), 7, 3),
+    (Workload("blk_decode_bf16q_fp8k_B3_G2", 3, 2, 5000, 64, 128, "bf16", "fp8", "ar1", "heavy", rho=0.98,
+              topk=100, group=2, seed=34), 64, 8),
+    (Workload("blk_bf16_L400_G32_block1", 1, 400, 400, 32, 64, "bf16", "bf16", "normal8", "heavy",
+              topk=20, group=32, seed=35), 1, 50),
+]
+
+
+def ulp_bf16(x):
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 7)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
+def test_block_route_parity(case):
+    wl, S_blk, n_sel = case
+    dev = cuda()
+    print(f"\n[block] {wl.name} block {S_blk} keep {n_sel}", flush=True)
+    inp = make_inputs(wl, dev)
+    a = dict(q_scale=inp["q_scale"], k_scale=inp["k_scale"], q_pos0=wl.q_pos0)
+    G = wl.group
+    cand, km, bsc, pq, pw = S.block_route(inp["q"], inp["k"], inp["w"], G, S_blk, n_sel, return_means=True,
+                                         return_scores=True, return_proxy=True, **a)
+    cand_ws = S.block_route(inp["q"], inp["k"], inp["w"], G, S_blk, n_sel, **a)
+    ridx = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, G, wl.topk, **a)
+    torch.cuda.synchronize()
+    srt = lambda x: torch.sort(x, dim=-1)[0]
+    assert torch.equal(srt(cand), srt(cand_ws))  # dump path and workspace path agree
+    q, k, w = real_inputs(inp)
+    km_f = km.float().cpu().numpy().astype(np.float64)
+    pq_f = pq.float().cpu().numpy().astype(np.float64)
+    pw_f = pw.cpu().numpy().astype(np.float64)
+    cand, bsc, ridx = cand.cpu().numpy(), bsc.cpu().numpy(), ridx.cpu().numpy()
+    lim = O.proxy_limits(wl.n_q, G, wl.q_pos0)
+    for b in range(wl.batch):
+        # block means and proxy: the rounded means
+        mean = O.block_means(k[b], S_blk)
+        qb, wb = O.proxy_means(q[b], w[b], G)
+        if wl.k_fmt == "f32":
+            assert np.allclose(km_f[b], mean, rtol=1e-6, atol=1e-7)
+        else:
+            ref, _ = O.round_proxy(mean, wb, "bf16")
+            assert (np.abs(km_f[b] - ref) <= ulp_bf16(ref) * 1.0001).all(), "block mean beyond 1 bf16 ulp"
+        if wl.q_fmt == "f32":
+            assert np.allclose(pq_f[b], qb, rtol=1e-6, atol=1e-7)
+        else:
+            ref, _ = O.round_proxy(qb, wb, "bf16")
+            assert (np.abs(pq_f[b] - ref) <= ulp_bf16(ref) * 1.0001).all(), "proxy beyond 1 bf16 ulp"
+        # block scores on the GPU's own proxy and block means
+        c_ora, B_ora, _ = O.block_route(pq_f[b], pw_f[b], km_f[b], lim, wl.n_k, S_blk, n_sel)
+        check_scores(bsc[b], B_ora, f"{wl.name} block scores b={b}")
+        # routing on the GPU's own block scores: exact (as sets)
+        c_own = []
+        n_full = (lim + 1) // S_blk
+        for g in range(cand.shape[1]):
+            f = int(n_full[g])
+            top = O.select_topk(bsc[b, g, :f].astype(np.float64), np.arange(f), n_sel)
+            keys = [np.arange(j * S_blk, (j + 1) * S_blk) for j in top]
+            keys.append(np.arange(f * S_blk, int(lim[g]) + 1))
+            c_own.append(np.concatenate(keys))
+        assert_same_sets(cand[b], c_own, f"{wl.name} candidates b={b}")
+        # Refine over the routed candidates: causal, distinct, -1 padded
+        check_rows_valid(ridx[b], wl.q_pos0 + np.arange(wl.n_q), wl.topk)
+        for t in range(wl.n_q):
+            got = sets(ridx[b, t : t + 1])[0]
+            assert got <= sets(cand[b, t // G : t // G + 1])[0]
+
+
+def test_all_blocks_kept_equals_dense():
+    dev = cuda()
+    wl = Workload("blk_all_bf16_L300_G20", 1, 300, 300, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98,
+                  topk=24, group=20, seed=36)
+    inp = make_inputs(wl, dev)
+    a = dict(q_scale=inp["q_scale"], k_scale=inp["k_scale"], q_pos0=wl.q_pos0)
+    cand = S.block_route(inp["q"], inp["k"], inp["w"], wl.group, 16, 300 // 16, **a)
+    refine = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, wl.group, wl.topk, **a)
+    dense = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **a)
+    torch.cuda.synchronize()
+    assert_same_sets(refine.cpu().numpy()[0], dense.cpu().numpy()[0], "refine(all blocks) vs dense")
