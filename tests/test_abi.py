@@ -134,3 +134,29 @@ def test_workspace_sizes_follow_the_layout(lib):
     br = lib.idx_workspace_bytes(ctypes.byref(p), 4, 10, 16, 3)
     n_b = -(-1000 // 16)
     assert br >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + n_b * 128 * 2 + 100 * 3 * 4 + 100 * n_b * 4
+
+
+def test_calibration_recall_matches_the_oracle_definition():
+    """The sweep's recall (torch, batched search) equals the oracle's set definition."""
+    import numpy as np
+    import torch
+    import oracle as O
+    from sparse_attention_token_causal_amd.calibrate import choose, recall
+    rng = np.random.default_rng(3)
+    exact = np.full((40, 16), -1, dtype=np.int32)
+    approx = np.full((40, 16), -1, dtype=np.int32)
+    for t in range(40):
+        n = int(rng.integers(1, 17))
+        e = rng.choice(200, size=n, replace=False)
+        exact[t, :n] = e
+        m = int(rng.integers(0, 17))
+        a = rng.choice(200, size=m, replace=False)
+        a[: m // 2] = e[: min(m // 2, n)][: m // 2] if m // 2 <= n else a[: m // 2]
+        a = np.unique(a)
+        approx[t, : a.size] = a
+    got = recall(torch.from_numpy(approx), torch.from_numpy(exact)).numpy()
+    assert np.allclose(got, O.recall(approx, exact))
+    rows = [dict(path="dense", recall_mean=1.0, ms=10.0), dict(path="a", recall_mean=0.95, ms=3.0),
+            dict(path="b", recall_mean=0.99, ms=5.0), dict(path="c", recall_mean=0.80, ms=1.0)]
+    assert choose(rows, 0.9)["path"] == "a" and choose(rows, 0.98)["path"] == "b"
+    assert choose(rows, 0.999) is None
