@@ -32,9 +32,12 @@ DEFAULT_WORKLOAD = "prefill_bf16_L32768_H64_d128_k2048"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
+# sources of the scan kernels whose HBM traffic the committed PMC runs measured
 KERNEL_SOURCES = ["sparse_attention_token_causal_amd/csrc/score.hip",
-                  "sparse_attention_token_causal_amd/csrc/common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+                  "sparse_attention_token_causal_amd/csrc/split.hip",
+                  "sparse_attention_token_causal_amd/csrc/common.hpp",
+                  "sparse_attention_token_causal_amd/csrc/kernels.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic.json")
 
 
 def log(*a):
@@ -59,14 +62,14 @@ def kernel_source_hash():
 
 
 def measured_traffic(workload):
-    """HBM bytes per score launch from committed rocprofv3 PMC runs, if they
-    were taken on the current kernel source for this workload; else None."""
+    """HBM bytes per scan launch from committed rocprofv3 PMC runs ({workload:
+    record}), if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel_source_sha") != kernel_source_hash() or rec.get("workload") != workload:
+    if not rec or rec.get("kernel_source_sha") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -240,6 +243,23 @@ def main():
     achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
     traffic = measured_traffic(wl.name)
+    roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic,
+            "kernel": "score (Q.K^T on MFMA + fused ReLU/weight/head-sum epilogue)",
+            "launch_ms": per_launch_ms, "flops_per_launch": flops_per_launch}
+    if kind == "decode":
+        # the decode scan streams the key cache: algorithmic bytes per launch =
+        # keys (+ per-token scales) + queries + head weights, each read once
+        kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_fmt]
+        qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_fmt]
+        key_bytes = wl.batch * wl.n_k * (wl.dim * kb + (4 if wl.k_fmt == "fp8" else 0))
+        q_bytes = wl.batch * wl.n_q * (wl.heads * wl.dim * qb + wl.heads * 4 + (4 if wl.q_fmt == "fp8" else 0))
+        alg = (key_bytes + q_bytes) / max(launches_per_step, 1e-9)
+        gbs = alg / (per_launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
+                "kernel": "split-key scan (streams the key cache; MFMA + fused epilogue)",
+                "launch_ms": per_launch_ms, "bytes_per_launch": alg, "flops_per_launch": flops_per_launch}
     result = {
         "metric": METRIC,
         "value": pairs / s_per_step,
@@ -259,14 +279,11 @@ def main():
         "queries_per_s": queries / s_per_step,
         "pairs_per_step": pairs,
         "kernels_ms_per_step": {k: v[0] / args.steps for k, v in prof.items() if v[1]},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "score (Q.K^T on MFMA + fused ReLU/weight/head-sum epilogue)",
-                     "launch_ms": per_launch_ms, "flops_per_launch": flops_per_launch},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     log(f"[bench] {result['ms_per_step']:.3f} ms/step, score {per_launch_ms:.3f} ms/launch "
-        f"({achieved:.1f} TFLOP/s, {100 * achieved / peak:.1f}% of {dtype} peak), select "
+        f"({roof['achieved']:.1f} {roof['unit']}, {100 * roof['frac']:.1f}% of the {roof['bound']} peak), select "
         f"{sel_ms / max(sel_n, 1):.3f} ms/launch")
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
