@@ -15,7 +15,9 @@ from .formats import (bf16_bits_to_f64, e4m3fn_bits_to_f64, f64_to_bf16_bits_rne
 from .indexer import (causal_scores, dense_scores, select_topk, dense_topk, proxy_means,
                       round_proxy, proxy_limits, proxy_scores, proxy_candidates,
                       refine_topk, reuse_topk, grouped_reference, recall,
-                      group_bounds, block_means, block_limits, block_route, block_reference)
+                      group_bounds, block_means, block_limits, block_route, block_reference,
+                      ivf_store, ivf_assign, ivf_update, ivf_build, ivf_visible_end,
+                      ivf_route, ivf_reference)
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "f64_to_bf16_bits_rne", "real_values",
@@ -23,4 +25,6 @@ __all__ = [
     "proxy_limits", "proxy_scores", "proxy_candidates", "refine_topk",
     "reuse_topk", "grouped_reference", "recall", "group_bounds",
     "block_means", "block_limits", "block_route", "block_reference",
+    "ivf_store", "ivf_assign", "ivf_update", "ivf_build", "ivf_visible_end",
+    "ivf_route", "ivf_reference",
 ]

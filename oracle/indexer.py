@@ -282,6 +282,136 @@ def block_reference(q, k, w, q_pos0, group, block, n_sel, topk, q_fmt, k_fmt):
 
 
 # ----------------------------------------------------------------------------
+# IVF routing with causal index versions (a third candidate generator)
+#
+# "AttentionIndex Architecture ...", "KEY FINDINGS", "An Inverted File With
+# Causal Versions" and "Worked Example: Blocks Lose, Clusters Win": keys are
+# grouped by similarity into inverted lists, a query is routed to the lists
+# whose representatives score highest and the native indexer re-scores their
+# members.  New keys become searchable at once and are added to the lists in
+# small batches; periodic refits regroup the whole prefix starting from the
+# previous clustering and publish a new version (lists and representatives
+# together); a query uses a version only if every key that built it lies in
+# its prefix.  Readings (the pages leave them open; no trained encoder here,
+# so representatives are plain means):
+#   * refits happen every R keys: version u (u = 1, 2, ...) is refit on keys
+#     [0, u R) by T Lloyd iterations of k-means with m centroids, starting
+#     from version u-1's centroids (version 1: the keys at positions
+#     floor(c R / m), c < m); one iteration assigns every key to its nearest
+#     stored centroid (squared L2, ties to the lower centroid) and replaces
+#     each centroid by the mean of its members (an empty cluster keeps its
+#     centroid);
+#   * centroids are stored like the proxy (``round_proxy``: bfloat16, float32
+#     for float32 keys) and assignment and routing both use the stored values;
+#   * between refits, new keys are added to version u's lists (nearest stored
+#     centroid, same rule) in batches of b keys counted from u R: a key
+#     becomes routable through its list once its batch is complete within the
+#     query's prefix; until then it is a candidate outright;
+#   * group g (prefix [0, p], p = pos of its last member) uses version
+#     u = floor((p + 1) / R); the keys [e, p] with e = u R + b floor((p + 1 - u R) / b)
+#     are always candidates (with no version, u = 0, e = 0: the whole prefix);
+#   * clusters are ranked by the indexer form of the group proxy against the
+#     stored centroid, ties to the lower centroid, and their visible members
+#     (keys < e) taken in that order while they fit in the budget C left next
+#     to the always-candidates; the first cluster that does not fit ends the walk.
+
+
+def ivf_store(x, k_fmt):
+    """A centroid as stored: float32 for float32 keys, bfloat16 (nearest even) otherwise."""
+    return round_proxy(x, np.zeros((1, 1)), k_fmt)[0]
+
+
+def ivf_assign(keys, cent):
+    """Index of the nearest centroid (squared L2) of each key; ties to the lower index."""
+    d2 = ((keys[:, None, :] - cent[None, :, :]) ** 2).sum(axis=2)
+    return np.argmin(d2, axis=1)
+
+
+def ivf_update(keys, assign, cent, k_fmt):
+    """One k-means update: each centroid becomes the stored mean of its members."""
+    new = cent.copy()
+    for c in range(cent.shape[0]):
+        members = keys[assign == c]
+        if members.shape[0] > 0:
+            new[c] = ivf_store(members.mean(axis=0), k_fmt)
+    return new
+
+
+def ivf_build(k, m, R, T, k_fmt):
+    """Versions u = 1..floor(n_k / R) of the index over one sequence's real keys k.
+
+    Returns a list of (centroids [m, d] as stored, assignment [n_k]) per
+    version: the nearest stored centroid of every key of the version's window
+    [0, min((u + 1) R, n_k)) - its refit keys and the keys added to its lists
+    until the next refit - and -1 beyond the window.
+    """
+    n_k = k.shape[0]
+    assert 1 <= m <= R
+    cent = ivf_store(np.stack([k[(c * R) // m] for c in range(m)]), k_fmt)
+    versions = []
+    for u in range(1, n_k // R + 1):
+        keys = k[: u * R]
+        for _ in range(T):
+            cent = ivf_update(keys, ivf_assign(keys, cent), cent, k_fmt)
+        end = min((u + 1) * R, n_k)
+        a = np.full(n_k, -1, dtype=np.int64)
+        a[:end] = ivf_assign(k[:end], cent)
+        versions.append((cent.copy(), a))
+    return versions
+
+
+def ivf_visible_end(last, R, b):
+    """Version used by a group whose last member sits at `last`, and the end e of its
+    routable keys: u = floor((last + 1) / R), e = u R + b floor((last + 1 - u R) / b)
+    (e = 0 without a version: there are no lists to add keys to)."""
+    u = (last + 1) // R
+    return u, (u * R + b * ((last + 1 - u * R) // b) if u >= 1 else 0)
+
+
+def ivf_route(qbar, wbar, versions, k_lim, R, b, n_cand):
+    """Candidates of each group ([n_g, n_cand] ascending, -1 padded), the cluster
+    scores [n_g, m] (-inf where the group has no version) and the clusters taken
+    ([n_g, m] in walk order, -1 padded).
+
+    qbar, wbar: stored proxies; versions: as ``ivf_build``; k_lim: pos(t_last) per group.
+    """
+    n_g = qbar.shape[0]
+    m = versions[0][0].shape[0] if versions else 1
+    S = np.full((n_g, m), -np.inf)
+    rows, taken = [], []
+    for g in range(n_g):
+        last = int(k_lim[g])
+        u, e = ivf_visible_end(last, R, b)
+        keys = [np.arange(e, last + 1)]
+        room = n_cand - keys[0].size
+        assert room >= 0, "budget below the always-candidate keys"
+        took = []
+        if u >= 1:
+            cent, a = versions[u - 1]
+            S[g] = np.maximum(cent @ qbar[g].T, 0.0) @ wbar[g]
+            for c in select_topk(S[g], np.arange(m), m):
+                members = np.nonzero(a[:e] == c)[0]
+                if members.size > room:
+                    break
+                keys.append(members)
+                took.append(c)
+                room -= members.size
+        rows.append(np.sort(np.concatenate(keys)))
+        taken.append(np.array(took, dtype=np.int64))
+    return _pad(rows, n_cand), S, _pad(taken, m)
+
+
+def ivf_reference(q, k, w, q_pos0, group, m, R, T, b, n_cand, topk, q_fmt, k_fmt):
+    """IVF index build, routing and Refine, entirely in the oracle, for one sequence."""
+    n_q = q.shape[0]
+    qbar, wbar = round_proxy(*proxy_means(q, w, group), q_fmt)
+    versions = ivf_build(k, m, R, T, k_fmt)
+    lim = proxy_limits(n_q, group, q_pos0)
+    cand, S, taken = ivf_route(qbar, wbar, versions, lim, R, b, n_cand)
+    return refine_topk(q, k, w, cand, group, q_pos0, topk), cand, S, versions
+
+
+# ----------------------------------------------------------------------------
 # measurement
 
 
