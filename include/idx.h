@@ -77,7 +77,9 @@ enum {
   IDX_OP_GROUP_PROXY_SCAN = 1,
   IDX_OP_REFINE_TOPK = 2,
   IDX_OP_REUSE_TOPK = 3,
-  IDX_OP_BLOCK_ROUTE = 4  /* n_cand = block size, topk = blocks kept */
+  IDX_OP_BLOCK_ROUTE = 4, /* n_cand = block size, topk = blocks kept */
+  IDX_OP_IVF_BUILD = 5,   /* n_cand = clusters per version; only the key fields of p are read */
+  IDX_OP_IVF_ROUTE = 6    /* group, n_cand = clusters per version */
 };
 
 /* One indexer problem: B sequences, each with n_q queries and n_k keys.
@@ -191,16 +193,81 @@ int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int3
                         void* out_proxy_q, float* out_proxy_w, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* IVF index with causal versions, a third candidate generator for
+ * idx_refine_topk ("AttentionIndex Architecture ...", "KEY FINDINGS" and "An
+ * Inverted File With Causal Versions": keys are grouped by similarity into
+ * inverted lists, a query is routed to the lists whose representatives score
+ * highest and the native indexer re-scores their members; new keys are added
+ * to the lists in small batches; periodic refits regroup the whole prefix
+ * starting from the previous clustering and publish a new version; a query
+ * uses a version only if every key that built it lies in its prefix).  The
+ * representatives here are plain means (no trained encoder).
+ *
+ * idx_ivf_build: for each sequence, versions u = 1 .. n_v = floor(n_k / R)
+ * (R = refit).  Version u is refit on keys [0, u R) by `iters` Lloyd
+ * iterations of k-means with m = n_clusters centroids, starting from version
+ * u-1's centroids (version 1: the keys at positions floor(c R / m)).  An
+ * iteration assigns each key to the nearest stored centroid (squared L2,
+ * ties to the lower centroid) and replaces each centroid by the mean of its
+ * members' real values (float32 sums; an empty cluster keeps its centroid).
+ * Centroids are stored as bfloat16 (round to nearest even), float32 for F32
+ * keys, and the stored values are what assignment and routing use.  The
+ * published lists of version u hold every key of its window
+ * [0, min((u + 1) R, n_k)) under its nearest centroid of version u, in key
+ * order within each list.  Only p->batch, n_k, dim, k_dtype, k and k_scale
+ * are read.  Outputs (n_tiles = ceil(n_k / 128)):
+ *   out_centroids [B, n_v, m, dim]   bfloat16 (float32 for F32 keys)
+ *   out_offsets   [B, n_v, m + 1]    int32: list c of version u is
+ *                 out_members[b, u-1, offsets[c] .. offsets[c+1]-1]
+ *   out_members   [B, n_v, n_k]      int32 (the first window-size entries used)
+ *   out_counts    [B, n_v, n_tiles + 1, m] int32: members of list c below key
+ *                 128 t (row n_tiles: the list sizes)
+ *   out_assign    optional [B, n_v, n_k] int32: the list of every key of the
+ *                 window, -1 beyond it.
+ * IDX_EINVAL for n_clusters outside [1, 1024], refit < n_clusters or not a
+ * multiple of 128, iters outside [0, 64], a null required output.  With
+ * n_k < R nothing is enqueued.  ws: idx_workspace_bytes(p, IDX_OP_IVF_BUILD,
+ * 0, n_clusters, 0).
+ *
+ * idx_ivf_route: group g (as in idx_group_proxy_scan, last member at
+ * position p_g) uses version u = floor((p_g + 1) / R).  Its routable keys end
+ * at e = u R + b floor((p_g + 1 - u R) / b) (b = insert_batch: keys join
+ * their lists in whole batches counted from the refit; e = 0 when u = 0);
+ * the keys [e, p_g] are candidates outright.  Clusters are ranked by
+ * sum_h wbar[h] * max(0, qbar[h,:] . centroid) with the stored proxy,
+ * descending, ties to the lower cluster, and taken in that order with their
+ * members below e while those fit in the n_cand - (p_g + 1 - e) slots left;
+ * the first cluster that does not fit ends the walk.
+ *   centroids/offsets/members/counts: the index idx_ivf_build wrote for the
+ *                 same keys, n_clusters and refit (unused when n_k < R).
+ *   out_cand      [B, n_g, n_cand] int32: the taken members (cluster by
+ *                 cluster), then the keys [e, p_g], then -1.
+ *   out_cluster_scores optional [B, n_g, m] float32, -inf without a version.
+ *   out_proxy_q/_w     optional, as in idx_group_proxy_scan.
+ * IDX_EINVAL also for insert_batch not a positive multiple of 128 or above
+ * refit, and n_cand < refit.  ws: idx_workspace_bytes(p, IDX_OP_IVF_ROUTE,
+ * group, n_clusters, 0). */
+int32_t idx_ivf_build(const idx_problem* p, int32_t n_clusters, int32_t refit, int32_t iters,
+                      void* out_centroids, int32_t* out_offsets, int32_t* out_members,
+                      int32_t* out_counts, int32_t* out_assign, void* ws, size_t ws_bytes,
+                      void* stream);
+int32_t idx_ivf_route(const idx_problem* p, int32_t group, int32_t n_clusters, int32_t refit,
+                      int32_t insert_batch, int32_t n_cand, const void* centroids,
+                      const int32_t* offsets, const int32_t* members, const int32_t* counts,
+                      int32_t* out_cand, float* out_cluster_scores, void* out_proxy_q,
+                      float* out_proxy_w, void* ws, size_t ws_bytes, void* stream);
+
 /* Kernel timing (measurement aid, off by default).  While enabled, every
  * kernel the library enqueues is bracketed by a pair of HIP events recorded
  * on the same stream; idx_profile_read synchronizes on the recorded events
  * and reports, per kernel kind, the summed duration in milliseconds and the
  * number of launches since the last read (then clears the records).
  * Kinds: 0 score (MFMA scan), 1 select (top-k), 2 proxy build, 3 reuse,
- * 4 fill (debug score dumps).  Returns IDX_EHIP on an event error.  Not
+ * 4 fill (debug score dumps), 5 IVF index build (the whole build), 6 IVF
+ * routing (cluster scores and list expansion).  Returns IDX_EHIP on an event error.  Not
  * reentrant: enable it from one host thread only. */
 enum { IDX_KERNEL_SCORE = 0, IDX_KERNEL_SELECT = 1, IDX_KERNEL_PROXY = 2, IDX_KERNEL_REUSE = 3,
-       IDX_KERNEL_FILL = 4, IDX_KERNEL_KINDS = 5 };
+       IDX_KERNEL_FILL = 4, IDX_KERNEL_IVF_BUILD = 5, IDX_KERNEL_IVF_ROUTE = 6, IDX_KERNEL_KINDS = 7 };
 int32_t idx_profile_enable(int32_t on);
 int32_t idx_profile_read(float* ms /* [IDX_KERNEL_KINDS] */, int32_t* launches /* [IDX_KERNEL_KINDS] */);
 

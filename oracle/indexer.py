@@ -368,12 +368,14 @@ def ivf_visible_end(last, R, b):
     return u, (u * R + b * ((last + 1 - u * R) // b) if u >= 1 else 0)
 
 
-def ivf_route(qbar, wbar, versions, k_lim, R, b, n_cand):
+def ivf_route(qbar, wbar, versions, k_lim, R, b, n_cand, scores=None):
     """Candidates of each group ([n_g, n_cand] ascending, -1 padded), the cluster
     scores [n_g, m] (-inf where the group has no version) and the clusters taken
     ([n_g, m] in walk order, -1 padded).
 
     qbar, wbar: stored proxies; versions: as ``ivf_build``; k_lim: pos(t_last) per group.
+    ``scores`` may supply precomputed cluster score rows (e.g. a GPU dump, to
+    check the walk exactly on the same values).
     """
     n_g = qbar.shape[0]
     m = versions[0][0].shape[0] if versions else 1
@@ -388,7 +390,10 @@ def ivf_route(qbar, wbar, versions, k_lim, R, b, n_cand):
         took = []
         if u >= 1:
             cent, a = versions[u - 1]
-            S[g] = np.maximum(cent @ qbar[g].T, 0.0) @ wbar[g]
+            if scores is None:
+                S[g] = np.maximum(cent @ qbar[g].T, 0.0) @ wbar[g]
+            else:
+                S[g] = np.asarray(scores[g], dtype=np.float64)
             for c in select_topk(S[g], np.arange(m), m):
                 members = np.nonzero(a[:e] == c)[0]
                 if members.size > room:

@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
 * ``group_proxy_scan``  PIVOT proxy per group + one shared prefix scan -> candidates
 * ``refine_topk``       PIVOT-Refine: per-query re-score of the group's candidates
 * ``reuse_topk``        PIVOT-Reuse: the group's shared top-k, causally filtered
+* ``block_route``       block-mean routing -> Refine candidates
+* ``ivf_build``         IVF index of the keys with causal versions
+* ``ivf_route``         IVF routing of the group proxies -> Refine candidates
 """
 
 import ctypes
@@ -23,6 +26,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsatc_idx
 
 IDX_F32, IDX_BF16, IDX_FP8_E4M3 = 0, 1, 2
 IDX_OP_SCORE_TOPK, IDX_OP_GROUP_PROXY_SCAN, IDX_OP_REFINE_TOPK, IDX_OP_REUSE_TOPK, IDX_OP_BLOCK_ROUTE = 0, 1, 2, 3, 4
+IDX_OP_IVF_BUILD, IDX_OP_IVF_ROUTE = 5, 6
+IVF_TILE = 128  # granularity of refit intervals, insert batches and the index's prefix counts
 
 _DTYPES = {torch.float32: IDX_F32, torch.bfloat16: IDX_BF16, torch.float8_e4m3fn: IDX_FP8_E4M3}
 
@@ -75,6 +80,10 @@ def load_library():
         lib.idx_reuse_topk.argtypes = [P, i32, vp, i32, vp, vp]
         lib.idx_block_route.restype = i32
         lib.idx_block_route.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.idx_ivf_build.restype = i32
+        lib.idx_ivf_build.argtypes = [P, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.idx_ivf_route.restype = i32
+        lib.idx_ivf_route.argtypes = [P, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.idx_profile_enable.restype = i32
         lib.idx_profile_enable.argtypes = [i32]
         lib.idx_profile_read.restype = i32
@@ -264,7 +273,81 @@ def block_route(q, k, w, group, block, n_sel, q_scale=None, k_scale=None, q_pos0
     return res[0] if len(res) == 1 else tuple(res)
 
 
-KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill")
+def ivf_build(k, n_clusters, refit, iters, k_scale=None, return_assign=False, workspace=None):
+    """IVF index with causal versions over keys k [B, n_k, d] (see idx_ivf_build).
+
+    Returns a dict with ``centroids`` [B, n_v, m, d] (bfloat16, float32 for
+    float32 keys), ``offsets`` [B, n_v, m + 1], ``members`` [B, n_v, n_k],
+    ``counts`` [B, n_v, ceil(n_k / 128) + 1, m] (int32), and with
+    ``return_assign`` the per-version cluster of every key of the window
+    ``assign`` [B, n_v, n_k] (-1 beyond it); plus the parameters.
+    n_v = n_k // refit may be 0 (then the arrays are empty).
+    """
+    lib = load_library()
+    if k.dim() != 3 or k.dtype not in _DTYPES:
+        raise IndexerError("expected k [B, n_k, d] in float32, bfloat16 or float8_e4m3fn")
+    if k_scale is not None and (k_scale.dtype != torch.float32 or tuple(k_scale.shape) != tuple(k.shape[:2])):
+        raise IndexerError("k_scale must be float32 [B, n_k]")
+    _need_gpu(k, k_scale)
+    B, n_k, d = k.shape
+    m = int(n_clusters)
+    n_v = n_k // int(refit) if refit > 0 else 0
+    nt = -(-n_k // IVF_TILE)
+    dev = k.device
+    p = _Problem(B, 0, n_k, 0, 0, d, 0, _DTYPES[k.dtype], None, None, _ptr(k), _ptr(k_scale), None)
+    cdt = torch.float32 if k.dtype == torch.float32 else torch.bfloat16
+    idx = dict(centroids=torch.empty((B, n_v, m, d), dtype=cdt, device=dev),
+               offsets=torch.empty((B, n_v, m + 1), dtype=torch.int32, device=dev),
+               members=torch.empty((B, n_v, n_k), dtype=torch.int32, device=dev),
+               counts=torch.empty((B, n_v, nt + 1, m), dtype=torch.int32, device=dev),
+               n_clusters=m, refit=int(refit), iters=int(iters))
+    asg = torch.empty((B, n_v, n_k), dtype=torch.int32, device=dev) if return_assign else None
+    n = int(lib.idx_workspace_bytes(ctypes.byref(p), IDX_OP_IVF_BUILD, 0, m, 0))
+    if workspace is not None and workspace.numel() < n:
+        raise IndexerError(f"workspace has {workspace.numel()} bytes, needs {n}")
+    ws = workspace if workspace is not None else torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    _check(lib.idx_ivf_build(ctypes.byref(p), m, int(refit), int(iters), _ptr(idx["centroids"]),
+                             _ptr(idx["offsets"]), _ptr(idx["members"]), _ptr(idx["counts"]), _ptr(asg),
+                             _ptr(ws), ws.numel(), _stream(dev)))
+    if return_assign:
+        idx["assign"] = asg
+    return idx
+
+
+def ivf_route(q, k, w, index, group, insert_batch, n_cand, q_scale=None, k_scale=None, q_pos0=None,
+              return_scores=False, return_proxy=False, workspace=None):
+    """IVF routing through ``index`` (from ``ivf_build`` on the same keys):
+    candidates int32 [B, n_g, n_cand] (-1 padded) for ``refine_topk``.
+
+    ``return_scores`` adds the cluster scores [B, n_g, m] (-inf without a
+    version); ``return_proxy`` adds the stored proxy q and w.
+    """
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    B, n_q, H, d = q.shape
+    n_g = -(-n_q // group)
+    m, R = index["n_clusters"], index["refit"]
+    cand = torch.empty((B, n_g, n_cand), dtype=torch.int32, device=q.device)
+    sc = torch.empty((B, n_g, m), dtype=torch.float32, device=q.device) if return_scores else None
+    pq = pw = None
+    if return_proxy:
+        pq = torch.empty((B, n_g, H, d), dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
+                         device=q.device)
+        pw = torch.empty((B, n_g, H), dtype=torch.float32, device=q.device)
+    ws = _workspace(p, IDX_OP_IVF_ROUTE, q.device, group, m, workspace=workspace)
+    _check(lib.idx_ivf_route(ctypes.byref(p), group, m, R, int(insert_batch), int(n_cand),
+                             _ptr(index["centroids"]), _ptr(index["offsets"]), _ptr(index["members"]),
+                             _ptr(index["counts"]), _ptr(cand), _ptr(sc), _ptr(pq), _ptr(pw), _ptr(ws),
+                             ws.numel(), _stream(q.device)))
+    res = [cand]
+    if return_scores:
+        res.append(sc)
+    if return_proxy:
+        res += [pq, pw]
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill", "ivf_build", "ivf_route")
 
 
 def profile_enable(on=True):
@@ -282,5 +365,5 @@ def profile_read():
 
 
 __all__ = ["profile_enable", "profile_read", "score_topk", "group_proxy_scan", "refine_topk", "reuse_topk",
-           "block_route", "make_problem",
+           "block_route", "ivf_build", "ivf_route", "make_problem",
            "workspace_bytes", "load_library", "library_path", "IndexerError"]

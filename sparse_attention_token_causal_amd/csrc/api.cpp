@@ -42,9 +42,9 @@ hipError_t timed(int kind, hipStream_t st, F launch) {
   if (!g_profile) return launch();
   TimedLaunch r{kind, take_event(), take_event()};
   if (!r.start || !r.stop) return hipErrorOutOfMemory;
-  hipEventRecord(r.start, st);
+  (void)hipEventRecord(r.start, st);
   hipError_t e = launch();
-  hipEventRecord(r.stop, st);
+  (void)hipEventRecord(r.stop, st);
   g_records.push_back(r);
   return e;
 }
@@ -454,6 +454,63 @@ BlockLayout block_layout(const idx_problem* p, int group, int block, int n_sel) 
   return L;
 }
 
+// IVF routing: centroids are stored like the proxy (float32 for float32
+// keys, bfloat16 otherwise); lists and counts are int32.
+int ivf_cent_dtype(const idx_problem* p) { return p->k_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
+size_t ivf_cent_elt(const idx_problem* p) { return ivf_cent_dtype(p) == IDX_F32 ? 4 : 2; }
+int ivf_tiles(int n) { return ceil_div(n, kIvfTile); }
+
+// Checks of the key fields an index build reads (q and w are not read).
+int check_keys(const idx_problem* p) {
+  if (!p) return IDX_EINVAL;
+  if (p->batch < 1 || p->n_k < 1 || p->dim < 1 || !dtype_ok(p->k_dtype) || !p->k) return IDX_EINVAL;
+  if ((p->k_dtype == IDX_FP8_E4M3) != (p->k_scale != nullptr)) return IDX_EINVAL;
+  if (!(p->dim == 64 || p->dim == 128)) return IDX_EUNSUPPORTED;
+  return IDX_OK;
+}
+
+bool ivf_params_ok(int m, int refit) {
+  return m >= 1 && m <= kIvfMaxClusters && refit >= m && refit % kIvfTile == 0;
+}
+
+// Build workspace: the initial centroids, per-key cluster and in-tile rank,
+// per-tile counts, and the lists of the assignment passes that are not
+// published (offsets, members, prefix counts).
+struct IvfBuildLayout {
+  size_t cur, rank, assign, tilecnt, counts, offsets, members, total;
+};
+
+IvfBuildLayout ivf_build_layout(const idx_problem* p, int m) {
+  const size_t B = p->batch, n_k = p->n_k, nt = ivf_tiles(p->n_k);
+  IvfBuildLayout L;
+  size_t o = 0;
+  L.cur = o;     o += align_up(B * m * p->dim * ivf_cent_elt(p));
+  L.rank = o;    o += align_up(B * n_k * 4);
+  L.assign = o;  o += align_up(B * n_k * 4);
+  L.tilecnt = o; o += align_up(B * nt * m * 4);
+  L.counts = o;  o += align_up(B * (nt + 1) * m * 4);
+  L.offsets = o; o += align_up(B * (m + 1) * 4);
+  L.members = o; o += align_up(B * n_k * 4);
+  L.total = o;
+  return L;
+}
+
+// Route workspace: the stored proxies and the cluster scores.
+struct IvfRouteLayout {
+  size_t pq, pw, scores, total;
+};
+
+IvfRouteLayout ivf_route_layout(const idx_problem* p, int group, int m) {
+  const int n_g = ceil_div(p->n_q, group);
+  IvfRouteLayout L;
+  size_t o = 0;
+  L.pq = o;     o += align_up(proxy_q_bytes(p, n_g));
+  L.pw = o;     o += align_up((size_t)p->batch * n_g * p->heads * 4);
+  L.scores = o; o += align_up((size_t)p->batch * n_g * m * 4);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -475,6 +532,10 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
                            int32_t topk) {
   (void)topk;
   if (op == IDX_OP_REUSE_TOPK) return 0;
+  if (op == IDX_OP_IVF_BUILD) {  // n_cand = clusters per version; only the key fields are read
+    if (check_keys(p) != IDX_OK || n_cand < 1 || n_cand > kIvfMaxClusters) return 0;
+    return ivf_build_layout(p, n_cand).total;
+  }
   if (check_problem(p) != IDX_OK) return 0;
   if (op == IDX_OP_SCORE_TOPK) {
     if (split_shape(p, p->n_q, p->q_dtype)) return split_layout(p, p->n_q).total;
@@ -492,6 +553,10 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
   if (op == IDX_OP_BLOCK_ROUTE) {  // n_cand = block size, topk = blocks kept
     if (n_cand < 1 || topk < 1) return 0;
     return block_layout(p, group, n_cand, topk).total;
+  }
+  if (op == IDX_OP_IVF_ROUTE) {  // n_cand = clusters per version
+    if (n_cand < 1 || n_cand > kIvfMaxClusters) return 0;
+    return ivf_route_layout(p, group, n_cand).total;
   }
   if (op == IDX_OP_REFINE_TOPK) {
     if (n_cand < 1) return 0;
@@ -696,6 +761,174 @@ int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int3
   if (rc != IDX_OK) return rc;
   if (timed(IDX_KERNEL_REUSE, st, [&] {
         return launch_block_expand(sel, p->batch, p->n_q, p->q_pos0, group, block, n_sel, out_cand, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  return IDX_OK;
+}
+
+int32_t idx_ivf_build(const idx_problem* p, int32_t n_clusters, int32_t refit, int32_t iters,
+                      void* out_centroids, int32_t* out_offsets, int32_t* out_members, int32_t* out_counts,
+                      int32_t* out_assign, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_keys(p);
+  if (rc != IDX_OK) return rc;
+  const int m = n_clusters, R = refit;
+  if (!ivf_params_ok(m, R) || iters < 0 || iters > 64) return IDX_EINVAL;
+  if (!out_centroids || !out_offsets || !out_members || !out_counts) return IDX_EINVAL;
+  const int n_v = p->n_k / R;
+  if (n_v == 0) return IDX_OK;  // no refit point inside the keys: nothing to publish
+  const IvfBuildLayout L = ivf_build_layout(p, m);
+  if (!ws || ws_bytes < L.total) return IDX_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int B = p->batch, n_k = p->n_k, D = p->dim, kf = p->k_dtype, nt = ivf_tiles(n_k);
+  const size_t eb = ivf_cent_elt(p);
+  const long long cent_bs = (long long)n_v * m * D, offs_bs = (long long)n_v * (m + 1);
+  const long long mem_bs = (long long)n_v * n_k, cnt_bs = (long long)n_v * (nt + 1) * m;
+  auto version_cent = [&](int u) { return (void*)((char*)out_centroids + (size_t)(u - 1) * m * D * eb); };
+
+  // One assignment pass over keys [0, n) with centroids (cent, bs) into the
+  // given lists (published when `pub` >= 1: that version's slots).
+  auto pass = [&](const void* cent, long long cbs, int n, int pub) {
+    IvfPassArgs a = {};
+    a.k = p->k;
+    a.k_scale = p->k_scale;
+    a.n_k = n_k;
+    a.m = m;
+    a.n_assign = n;
+    a.cent = cent;
+    a.cent_bs = cbs;
+    a.rank = (int*)(base + L.rank);
+    a.rank_bs = n_k;
+    a.tilecnt = (int*)(base + L.tilecnt);
+    a.tilecnt_bs = (long long)nt * m;
+    if (pub >= 1) {
+      a.assign = out_assign ? out_assign + (size_t)(pub - 1) * n_k : (int*)(base + L.assign);
+      a.assign_bs = out_assign ? mem_bs : n_k;
+      a.counts = out_counts + (size_t)(pub - 1) * (nt + 1) * m;
+      a.counts_bs = cnt_bs;
+      a.offsets = out_offsets + (size_t)(pub - 1) * (m + 1);
+      a.offsets_bs = offs_bs;
+      a.members = out_members + (size_t)(pub - 1) * n_k;
+      a.members_bs = mem_bs;
+    } else {
+      a.assign = (int*)(base + L.assign);
+      a.assign_bs = n_k;
+      a.counts = (int*)(base + L.counts);
+      a.counts_bs = (long long)(nt + 1) * m;
+      a.offsets = (int*)(base + L.offsets);
+      a.offsets_bs = m + 1;
+      a.members = (int*)(base + L.members);
+      a.members_bs = n_k;
+    }
+    return launch_ivf_pass(a, kf, D, B, st);
+  };
+  auto update = [&](const void* src, long long sbs, void* dst, const int* offs, long long obs, const int* mem,
+                    long long mbs, int copy_only) {
+    IvfUpdateArgs a = {};
+    a.k = p->k;
+    a.k_scale = p->k_scale;
+    a.n_k = n_k;
+    a.m = m;
+    a.copy_only = copy_only;
+    a.offsets = offs;
+    a.offsets_bs = obs;
+    a.members = mem;
+    a.members_bs = mbs;
+    a.src = src;
+    a.src_bs = sbs;
+    a.dst = dst;
+    a.dst_bs = cent_bs;
+    return launch_ivf_update(a, kf, D, B, st);
+  };
+
+  return timed(IDX_KERNEL_IVF_BUILD, st, [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    if (out_assign) {
+      e = launch_fill_i32(out_assign, (size_t)B * n_v * n_k, -1, st);
+      if (e != hipSuccess) return e;
+    }
+    e = launch_ivf_init(p->k, p->k_scale, kf, B, n_k, D, m, R, base + L.cur, (long long)m * D, st);
+    if (e != hipSuccess) return e;
+    const void* prev = base + L.cur;
+    long long prev_bs = (long long)m * D;
+    for (int u = 1; u <= n_v; ++u) {
+      void* dst = version_cent(u);
+      for (int it = 0; it < iters; ++it) {
+        const void* src = it == 0 ? prev : dst;
+        const long long sbs = it == 0 ? prev_bs : cent_bs;
+        if (it == 0 && u > 1) {
+          // the lists published for version u-1 are the assignment of keys
+          // [0, u R) to its centroids: this iteration's assignment
+          e = update(src, sbs, dst, out_offsets + (size_t)(u - 2) * (m + 1), offs_bs,
+                     out_members + (size_t)(u - 2) * n_k, mem_bs, 0);
+        } else {
+          e = pass(src, sbs, u * R, 0);
+          if (e == hipSuccess)
+            e = update(src, sbs, dst, (int*)(base + L.offsets), m + 1, (int*)(base + L.members), n_k, 0);
+        }
+        if (e != hipSuccess) return e;
+      }
+      if (iters == 0) {
+        e = update(prev, prev_bs, dst, (int*)(base + L.offsets), m + 1, (int*)(base + L.members), n_k, 1);
+        if (e != hipSuccess) return e;
+      }
+      e = pass(dst, cent_bs, std::min((long long)(u + 1) * R, (long long)n_k), u);
+      if (e != hipSuccess) return e;
+      prev = dst;
+      prev_bs = cent_bs;
+    }
+    return hipSuccess;
+  }) != hipSuccess ? IDX_EHIP : IDX_OK;
+}
+
+int32_t idx_ivf_route(const idx_problem* p, int32_t group, int32_t n_clusters, int32_t refit,
+                      int32_t insert_batch, int32_t n_cand, const void* centroids, const int32_t* offsets,
+                      const int32_t* members, const int32_t* counts, int32_t* out_cand,
+                      float* out_cluster_scores, void* out_proxy_q, float* out_proxy_w, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  const int m = n_clusters, R = refit;
+  if (group < 1 || !ivf_params_ok(m, R) || !out_cand) return IDX_EINVAL;
+  if (insert_batch < kIvfTile || insert_batch % kIvfTile != 0 || insert_batch > R || n_cand < R) return IDX_EINVAL;
+  const int n_v = p->n_k / R;
+  if (n_v >= 1 && (!centroids || !offsets || !members || !counts)) return IDX_EINVAL;
+  const int pqf = proxy_q_dtype(p);
+  if (!combo_supported(pqf, ivf_cent_dtype(p), p->heads, p->dim)) return IDX_EUNSUPPORTED;
+  const IvfRouteLayout L = ivf_route_layout(p, group, m);
+  if (!ws || ws_bytes < L.total) return IDX_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int n_g = ceil_div(p->n_q, group);
+  void* pq = out_proxy_q ? out_proxy_q : (void*)(base + L.pq);
+  float* pw = out_proxy_w ? out_proxy_w : (float*)(base + L.pw);
+  if (timed(IDX_KERNEL_PROXY, st, [&] {
+        return launch_proxy_build(p->q, p->q_scale, p->w, p->batch, p->n_q, p->heads, p->dim, p->q_dtype,
+                                  group, pq, pw, st);
+      }) != hipSuccess)
+    return IDX_EHIP;
+  IvfRouteArgs a = {};
+  a.pq = pq;
+  a.pw = pw;
+  a.cents = centroids;
+  a.offsets = offsets;
+  a.members = members;
+  a.counts = counts;
+  a.n_v = n_v;
+  a.m = m;
+  a.n_k = p->n_k;
+  a.n_tiles = ivf_tiles(p->n_k);
+  a.n_g = n_g;
+  a.n_q = p->n_q;
+  a.q_pos0 = p->q_pos0;
+  a.group = group;
+  a.refit = R;
+  a.batch = insert_batch;
+  a.n_cand = n_cand;
+  a.scores = out_cluster_scores ? out_cluster_scores : (float*)(base + L.scores);
+  a.cand = out_cand;
+  if (timed(IDX_KERNEL_IVF_ROUTE, st, [&] {
+        return launch_ivf_route(a, pqf, p->heads, p->dim, p->batch, st);
       }) != hipSuccess)
     return IDX_EHIP;
   return IDX_OK;

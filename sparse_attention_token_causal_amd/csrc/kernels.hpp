@@ -172,4 +172,65 @@ hipError_t launch_block_means(const void* k, const float* k_scale, int B, int n_
 hipError_t launch_block_expand(const int* sel, int B, int n_q, int q_pos0, int group, int block,
                                int n_sel, int* cand, hipStream_t st);
 
+// IVF routing (see ivf.hip).
+constexpr int kIvfTile = 128;          // keys per assignment workgroup; granularity of the prefix counts
+constexpr int kIvfMaxClusters = 1024;  // clusters per version
+
+// One assignment pass over keys [0, n_assign) of every sequence: nearest
+// centroid, then the stable inverted lists.  *_bs: per-sequence strides in
+// elements.
+struct IvfPassArgs {
+  const void* k;          // [B, n_k, D]
+  const float* k_scale;   // [B, n_k] (FP8 keys only)
+  int n_k, m, n_assign;
+  const void* cent;       // [m, D] stored centroids (bfloat16, float32 for float32 keys)
+  long long cent_bs;
+  int* assign;            // [n_assign] nearest centroid
+  long long assign_bs;
+  int* rank;              // [n_assign] rank among the same-cluster keys of its 128-key tile
+  long long rank_bs;
+  int* tilecnt;           // [n_tiles, m] keys per (tile, cluster)
+  long long tilecnt_bs;
+  int* counts;            // [n_tiles + 1, m] members in tiles before t; row n_tiles = list sizes
+  long long counts_bs;
+  int* offsets;           // [m + 1] list starts
+  long long offsets_bs;
+  int* members;           // [n_assign] keys grouped by cluster, ascending within a list
+  long long members_bs;
+};
+
+struct IvfUpdateArgs {
+  const void* k;
+  const float* k_scale;
+  int n_k, m;
+  int copy_only;          // 1: dst = src for every cluster
+  const int* offsets;     // lists of the assignment to src
+  long long offsets_bs;
+  const int* members;
+  long long members_bs;
+  const void* src;        // [m, D] stored centroids before the update
+  long long src_bs;
+  void* dst;              // [m, D] after (may equal src)
+  long long dst_bs;
+};
+
+struct IvfRouteArgs {
+  const void* pq;         // [B, n_g, H, D] stored proxies
+  const float* pw;        // [B, n_g, H]
+  const void* cents;      // index: [B, n_v, m, D]
+  const int* offsets;     // index: [B, n_v, m + 1]
+  const int* members;     // index: [B, n_v, n_k]
+  const int* counts;      // index: [B, n_v, n_tiles + 1, m]
+  int n_v, m, n_k, n_tiles, n_g, n_q, q_pos0, group, refit, batch, n_cand;
+  float* scores;          // [B, n_g, m] cluster scores (-inf without a version)
+  int* cand;              // [B, n_g, n_cand]
+};
+
+hipError_t launch_fill_i32(int* p, size_t n, int v, hipStream_t st);
+hipError_t launch_ivf_init(const void* k, const float* k_scale, int kf, int B, int n_k, int D, int m, int R,
+                           void* dst, long long dst_bs, hipStream_t st);
+hipError_t launch_ivf_pass(const IvfPassArgs& a, int kf, int D, int B, hipStream_t st);
+hipError_t launch_ivf_update(const IvfUpdateArgs& a, int kf, int D, int B, hipStream_t st);
+hipError_t launch_ivf_route(const IvfRouteArgs& a, int cf, int H, int D, int B, hipStream_t st);
+
 }  // namespace idx

@@ -12,7 +12,11 @@ top-k tokens and scores are long-tailed along the key axis):
   q_t = rho * q_{t-1} + eps_t with eps ~ N(0,1) i.i.d. per (head, dim) and
   q_0 drawn from the stationary N(0, 1/(1-rho^2));
 * keys: either i.i.d. N(0,1)/8, or N(0,1) with floor(n_k/100) randomly
-  chosen rows scaled by 4 (heavy-tailed keys);
+  chosen rows scaled by 4 (heavy-tailed keys), or similarity groups
+  scattered over positions ("clustered": `clusters` centers ~ N(0,1), each
+  key = its group's center + spread * N(0,1), groups drawn uniformly per
+  position; with seed_stride > 0 the key at position c * seed_stride belongs
+  to group c, for c < clusters);
 * head weights: U(0,1).
 
 Two further structures exist only to exercise the select's tie handling:
@@ -51,6 +55,9 @@ class Workload:
     n_cand: int = 0
     seed: int = 0
     w_dist: str = "uniform"  # "uniform" | "int" | "signed" (U(-1, 1): scores can be negative)
+    clusters: int = 0        # "clustered" keys: number of groups
+    spread: float = 0.1      # "clustered" keys: within-group noise
+    seed_stride: int = 0     # "clustered" keys: position c * seed_stride holds group c
 
     @property
     def q_pos0(self):
@@ -137,6 +144,15 @@ def make_inputs(wl: Workload, device="cpu"):
         for b in range(B):
             rows = torch.randperm(nk, generator=g, device=device)[:n_heavy]
             k[b, rows] *= 4.0
+    elif wl.k_dist == "clustered":
+        C = wl.clusters
+        centers = torch.randn((B, C, d), generator=g, device=device, dtype=torch.float32)
+        owner = torch.randint(0, C, (B, nk), generator=g, device=device)
+        if wl.seed_stride > 0:
+            pos = torch.arange(C, device=device) * wl.seed_stride
+            keep = pos < nk
+            owner[:, pos[keep]] = torch.arange(C, device=device)[keep]
+        k = torch.gather(centers, 1, owner[..., None].expand(B, nk, d)) + wl.spread * k
     else:
         raise ValueError(wl.k_dist)
     w = torch.rand((B, nq, H), generator=g, device=device, dtype=torch.float32)

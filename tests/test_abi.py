@@ -27,7 +27,8 @@ def lib():
 def test_header_declares_the_four_entry_points():
     fns = declared_functions()
     for f in ("idx_score_topk", "idx_group_proxy_scan", "idx_refine_topk", "idx_reuse_topk",
-              "idx_block_route", "idx_workspace_bytes", "idx_status_string", "idx_version"):
+              "idx_block_route", "idx_ivf_build", "idx_ivf_route", "idx_workspace_bytes", "idx_status_string",
+              "idx_version"):
         assert f in fns
 
 
@@ -93,6 +94,58 @@ def test_invalid_call_arguments(lib):
                                None) == -1
     assert lib.idx_block_route(ctypes.byref(problem(q=None)), 4, 8, 2, FAKE, None, None, None, None, None, 0,
                                None) == -1
+
+
+def ivf_build_call(lib, p, m=64, R=256, T=2, outs=(FAKE, FAKE, FAKE, FAKE), ws=FAKE, ws_bytes=1 << 40):
+    return lib.idx_ivf_build(ctypes.byref(p), m, R, T, *outs, None, ws, ws_bytes, None)
+
+
+def ivf_route_call(lib, p, G=4, m=64, R=256, b=128, C=512, index=(FAKE, FAKE, FAKE, FAKE), out=FAKE, ws=FAKE,
+                   ws_bytes=1 << 40):
+    return lib.idx_ivf_route(ctypes.byref(p), G, m, R, b, C, *index, out, None, None, None, ws, ws_bytes, None)
+
+
+def test_ivf_invalid_arguments(lib):
+    p = problem(n_q=512, n_k=512)
+    # build: clusters in [1, 1024], refit >= clusters and a multiple of 128, iterations in [0, 64]
+    for m, R, T in ((0, 256, 1), (1025, 2048, 1), (300, 256, 1), (64, 200, 1), (64, 256, -1), (64, 256, 65)):
+        assert ivf_build_call(lib, p, m, R, T) == -1, (m, R, T)
+    for i in range(4):
+        outs = [FAKE] * 4
+        outs[i] = None
+        assert ivf_build_call(lib, p, outs=tuple(outs)) == -1
+    assert ivf_build_call(lib, problem(n_q=512, n_k=512, k=None)) == -1
+    assert ivf_build_call(lib, problem(n_q=512, n_k=512, dim=96)) == -2
+    # the build reads only the keys: q and w may be absent
+    assert ivf_build_call(lib, problem(n_q=512, n_k=512, q=None, w=None), ws=None, ws_bytes=0) == -3
+    # route: group, batch a multiple of 128 within refit, budget >= refit, index present, output
+    assert ivf_route_call(lib, p, G=0) == -1
+    for b in (0, 64, 200, 384):
+        assert ivf_route_call(lib, p, b=b) == -1, b
+    assert ivf_route_call(lib, p, C=255) == -1
+    assert ivf_route_call(lib, p, out=None) == -1
+    for i in range(4):
+        index = [FAKE] * 4
+        index[i] = None
+        assert ivf_route_call(lib, p, index=tuple(index)) == -1
+    # no version inside the keys (n_k < refit): the index is not needed
+    short = problem(n_q=100, n_k=100)
+    assert ivf_route_call(lib, short, index=(None,) * 4, ws=None, ws_bytes=0) == -3
+    assert ivf_build_call(lib, short, ws=None, ws_bytes=0) == 0  # nothing to build, nothing enqueued
+
+
+def test_ivf_workspace_sizes(lib):
+    p = problem(n_q=1000, n_k=1000)
+    nb = lib.idx_workspace_bytes(ctypes.byref(p), 5, 0, 64, 0)
+    nt = -(-1000 // 128)
+    # initial centroids (bf16), rank, assignment, tile counts, prefix counts, offsets, members
+    assert nb >= 64 * 128 * 2 + 2 * 1000 * 4 + nt * 64 * 4 + (nt + 1) * 64 * 4 + 65 * 4 + 1000 * 4
+    assert lib.idx_workspace_bytes(ctypes.byref(p), 5, 0, 0, 0) == 0
+    assert lib.idx_workspace_bytes(ctypes.byref(p), 5, 0, 1025, 0) == 0
+    nr = lib.idx_workspace_bytes(ctypes.byref(p), 6, 10, 64, 0)
+    assert nr >= 100 * 64 * 128 * 2 + 100 * 64 * 4 + 100 * 64 * 4
+    assert ivf_build_call(lib, p, m=64, R=256, ws_bytes=nb - 1) == -3
+    assert ivf_route_call(lib, p, G=10, m=64, R=256, ws_bytes=nr - 1) == -3
 
 
 def test_workspace_checks(lib):
