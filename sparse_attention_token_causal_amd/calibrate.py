@@ -3,8 +3,10 @@
 ``python -m sparse_attention_token_causal_amd.calibrate`` runs, on seeded
 synthetic prefill inputs of one or more lengths, the dense indexer (the
 exact top-k), PIVOT-Refine and PIVOT-Reuse over a grid of (group size G,
-candidate budget C), and block-mean routing + Refine over a grid of (block
-size, blocks kept), all through the library's C ABI on one GPU.  For every
+candidate budget C), block-mean routing + Refine over a grid of (block
+size, blocks kept), and IVF routing + Refine over a grid of (clusters,
+refit interval, Lloyd iterations, insert batch, budget) - the index build
+timed with the path - all through the library's C ABI on one GPU.  For every
 setting it reports the recall of the dense top-k (mean and minimum over the
 queries) and the time of the whole path, and picks the cheapest setting that
 reaches a recall target.
@@ -21,7 +23,9 @@ What the pages ask for that this measures:
   calibration, a sweep against the dense top-k on synthetic inputs).
 * "AttentionIndex Architecture ...", "KEY FINDINGS" and "Why Positional
   Blocks Lose Recall": at a fixed candidate budget the recall of contiguous
-  block routing decays as the context grows.
+  block routing decays as the context grows; grouping keys by similarity
+  (an inverted file, "An Inverted File With Causal Versions") is the fix
+  the page describes.
 
 Recall is |S_t & D_t| / |D_t| with D_t the dense top-k of query t, computed
 on the GPU with a sort and a batched binary search.  This is measurement
@@ -34,7 +38,7 @@ import sys
 
 import torch
 
-from . import block_route, group_proxy_scan, refine_topk, reuse_topk, score_topk
+from . import block_route, group_proxy_scan, ivf_build, ivf_route, refine_topk, reuse_topk, score_topk
 from .synth import Workload, make_inputs
 
 
@@ -61,16 +65,21 @@ def _timed(fn, reps):
     return out, t0.elapsed_time(t1) / reps
 
 
-def workload(L, seed=0, rho=0.98, topk=2048):
-    """The 32K-token prefill recipe at length L (bf16, AR(1) queries, heavy-tailed keys)."""
-    return Workload(f"calib_bf16_L{L}", 1, L, L, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=rho,
-                    topk=topk, seed=seed)
+def workload(L, seed=0, rho=0.98, topk=2048, keys="heavy", key_groups=0):
+    """The 32K-token prefill recipe at length L (bf16, AR(1) queries, heavy-tailed keys);
+    ``keys="clustered"`` swaps in `key_groups` similarity groups scattered over positions."""
+    return Workload(f"calib_bf16_L{L}", 1, L, L, 64, 128, "bf16", "bf16", "ar1", keys, rho=rho,
+                    topk=topk, seed=seed, clusters=key_groups, spread=0.5)
 
 
-def sweep(L, pivot_grid, block_grid, reps=2, seed=0, dev=None):
-    """Rows of {path, L, setting, budget, recall_mean, recall_min, ms} for one length."""
+def sweep(L, pivot_grid, block_grid, ivf_grid=(), reps=2, seed=0, dev=None, keys="heavy", key_groups=0):
+    """Rows of {path, L, setting, budget, recall_mean, recall_min, ms} for one length.
+
+    ivf_grid: (G, clusters, refit, iterations, insert batch, budget) tuples;
+    their ``ms`` includes the index build, also reported alone as ``build_ms``.
+    """
     dev = dev or torch.device("cuda:0")
-    wl = workload(L, seed)
+    wl = workload(L, seed, keys=keys, key_groups=key_groups)
     inp = make_inputs(wl, dev)
     q, k, w = inp["q"], inp["k"], inp["w"]
     K = wl.topk
@@ -100,6 +109,14 @@ def sweep(L, pivot_grid, block_grid, reps=2, seed=0, dev=None):
             return refine_topk(q, k, w, cand, G, K)
         idx, ms = _timed(blocks, reps)
         add("block-refine", f"G={G} block={blk} keep={keep}", blk * keep, idx, ms)
+    for G, m, R, T, b, C in ivf_grid:
+        def ivf():
+            index = ivf_build(k, m, R, T)
+            cand = ivf_route(q, k, w, index, G, b, C)
+            return refine_topk(q, k, w, cand, G, K)
+        idx, ms = _timed(ivf, reps)
+        add("ivf-refine", f"G={G} m={m} R={R} T={T} b={b}", C, idx, ms)
+        _, rows[-1]["build_ms"] = _timed(lambda: ivf_build(k, m, R, T), reps)
     return rows
 
 
@@ -115,8 +132,15 @@ def main(argv=None):
     ap.add_argument("--groups", default="16,64")
     ap.add_argument("--budgets", default="4096,8192,16384")
     ap.add_argument("--block", type=int, default=64)
+    ap.add_argument("--clusters", default="256", help="IVF clusters per version (comma list)")
+    ap.add_argument("--refit", type=int, default=4096, help="IVF refit interval (keys)")
+    ap.add_argument("--iters", type=int, default=2, help="IVF Lloyd iterations per refit")
+    ap.add_argument("--insert-batch", type=int, default=512, help="IVF insert batch (keys)")
     ap.add_argument("--target", type=float, default=0.9)
     ap.add_argument("--reps", type=int, default=2)
+    ap.add_argument("--keys", default="heavy", choices=["heavy", "clustered"],
+                    help="key distribution: heavy-tailed i.i.d. rows, or similarity groups scattered over positions")
+    ap.add_argument("--key-groups", type=int, default=512, help="similarity groups of the clustered keys")
     ap.add_argument("--json", action="store_true", help="one JSON object per line instead of a table")
     a = ap.parse_args(argv)
     groups = [int(x) for x in a.groups.split(",")]
@@ -125,14 +149,18 @@ def main(argv=None):
     for L in (int(x) for x in a.lengths.split(",")):
         pivot = [(G, C) for G in groups for C in budgets if C < L]
         blocks = [(G, a.block, C // a.block) for G in groups for C in budgets if C < L]
-        rows = sweep(L, pivot, blocks, reps=a.reps)
+        ivfs = [(G, int(m), a.refit, a.iters, a.insert_batch, C) for G in groups for m in a.clusters.split(",")
+                for C in budgets if a.refit <= C < L]
+        rows = sweep(L, pivot, blocks, ivfs, reps=a.reps, keys=a.keys, key_groups=a.key_groups)
         all_rows += rows
         for r in rows:
             if a.json:
                 print(json.dumps(r), flush=True)
             else:
-                print(f"L={r['L']:7d} {r['path']:13s} {r['setting']:26s} budget {r['budget']:7d}  "
-                      f"recall {r['recall_mean']:.4f} (min {r['recall_min']:.4f})  {r['ms']:8.2f} ms", flush=True)
+                extra = f"  (index build {r['build_ms']:.2f} ms)" if "build_ms" in r else ""
+                print(f"L={r['L']:7d} {r['path']:13s} {r['setting']:30s} budget {r['budget']:7d}  "
+                      f"recall {r['recall_mean']:.4f} (min {r['recall_min']:.4f})  {r['ms']:8.2f} ms{extra}",
+                      flush=True)
         best = choose(rows, a.target)
         print(f"L={L}: fastest setting with mean recall >= {a.target}: "
               f"{'none' if best is None else best['path'] + ' ' + best['setting']}", flush=True)

@@ -109,15 +109,17 @@ def test_all_blocks_kept_equals_dense():
 
 
 def test_calibration_sweep_small():
-    """The (G, C) / block sweep runs end to end: dense recall 1, every recall in [0, 1],
+    """The (G, C) / block / IVF sweep runs end to end: dense recall 1, every recall in [0, 1],
     and a budget that covers the whole prefix recovers the dense top-k exactly."""
     from sparse_attention_token_causal_amd.calibrate import choose, sweep
     cuda()
     L = 1024
-    rows = sweep(L, [(16, 256), (16, L)], [(16, 32, 8), (16, 32, L // 32)], reps=1)
+    rows = sweep(L, [(16, 256), (16, L)], [(16, 32, 8), (16, 32, L // 32)],
+                 [(16, 32, 256, 2, 128, 512), (16, 32, 256, 2, 128, L)], reps=1)
     assert rows[0]["path"] == "dense" and rows[0]["recall_mean"] == 1.0
     for r in rows:
         assert 0.0 <= r["recall_min"] <= r["recall_mean"] <= 1.0 and r["ms"] > 0
     full = [r for r in rows if r["budget"] >= L and r["path"] != "dense"]
     assert full and all(r["recall_min"] == 1.0 for r in full)
     assert choose(rows, 1.0) is not None
+    assert any(r["path"] == "ivf-refine" and r["build_ms"] > 0 for r in rows)
