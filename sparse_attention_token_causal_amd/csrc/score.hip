@@ -306,12 +306,15 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   }
 
 
-  // ---- epilogue of one block: ReLU, x w, sum over heads, scale, mask, store ----
+  // ---- epilogue: ReLU, x w, sum over heads, scale, mask, store ----
   // The head sum is an in-lane weighted sum over the 16 result rows the lane
-  // holds, plus the other half-wave's partial (v_permlane32_swap).  Lanes
-  // 0-31 store column block 0 and lanes 32-63 block 1; `key`/`scale` describe
-  // this lane's column (kw*64 + half*32 + lane%32) of tile c0.
-  auto epilogue = [&](int cb, int c0, int key, float scale, bool live) {
+  // holds (`partial`, one 32-column block), plus the other half-wave's
+  // partial.  One v_permlane32_swap of the two blocks' partials leaves lane
+  // l < 32 with both halves of block 0's column l and lane l >= 32 with both
+  // halves of block 1's column l - 32, so the rest of the epilogue (mask,
+  // scale, store or filter) runs once per tile on 64 distinct columns:
+  // lane l owns column kw*64 + l of tile c0, described by `key`/`scale`.
+  auto partial = [&](int cb, float* pout) {
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
       float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four independent FMA chains
@@ -322,18 +325,27 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
           if ((32 * rb + 8 * (v / 4)) / H == qi) {
             // ReLU as an integer max of the bits: negative floats (and -0)
             // are negative integers, so they become +0 (one VALU op, no
-            // NaN canonicalisation; the MFMA results are finite)
+            // NaN canonicalisation)
             const float r = __int_as_float(max(__float_as_int(acc[rb][cb][v]), 0));
             ps[v & 3] = __builtin_fmaf(wreg[rb][v], r, ps[v & 3]);
           }
-      const float p = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
-      const float other = __uint_as_float(cb == 0 ? sw[1] : sw[0]);
-      const float tot = p + other;
+      pout[qi] = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    }
+  };
+  // last visible key of each of this wave's queries (-1 past the row range)
+  int qlim[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) qlim[qi] = t_first + qi < r_end ? row_limit(a, t_first + qi) : -1;
+  auto epilogue = [&](const float* p0, const float* p1, int c0, int key, float scale, bool live) {
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0[qi]), __float_as_uint(p1[qi]), false,
+                                                       false);
+      const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       const int t = t_first + qi;
-      const int col = c0 + kw * 64 + half * 32 + l32;
-      const bool mine = live && half == cb && t < r_end && col < c_end;
-      const bool ok = mine && key >= 0 && key <= row_limit(a, t);
+      const int col = c0 + kw * 64 + l;
+      const bool mine = live && t < r_end && col < c_end;
+      const bool ok = mine && key >= 0 && key <= qlim[qi];
       const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
       if constexpr (!FILTER) {
         if (mine) a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
@@ -407,7 +419,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   __syncthreads();
   int buf = 0, prev_c0 = c_begin, key_prev = -1;
   float scale_prev = 1.f;
-  const int jl = kw * 64 + half * 32 + l32;
+  float p0_prev[QW], p1[QW];  // partial head sums of the previous tile's blocks
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) p0_prev[qi] = 0.f;
+  const int jl = kw * 64 + l;
   auto tile = [&](auto par_c, int c0) {
     constexpr int PAR = decltype(par_c)::value;  // parity of this tile's index
     using Cur = std::integral_constant<int, PAR>;
@@ -421,15 +436,16 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       scale_cur = ((const float*)(ck + TW))[jl];
     }
     if constexpr (PRELOAD) load_block(bfA, buf, 0);
-    // block 0 MFMAs || block 1 epilogue of the previous tile (nothing is
-    // stored on the first tile) || block 1 fragment reads
+    // block 0 MFMAs || the previous tile's block 1 partials and its epilogue
+    // (nothing is stored on the first tile) || block 1 fragment reads
     mfma_block(bfA, buf, 0);
-    epilogue(1, prev_c0, key_prev, scale_prev, c0 != c_begin);
+    partial(1, p1);
+    epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, c0 != c_begin);
     if constexpr (PRELOAD) load_block(bfB, buf, 1);
     IDX_INTERLEAVE(0, true);
-    // block 1 MFMAs || block 0 epilogue
+    // block 1 MFMAs || block 0 partials
     mfma_block(bfB, buf, 1);
-    epilogue(0, c0, key_cur, scale_cur, true);
+    partial(0, p0_prev);
     IDX_INTERLEAVE(1, false);
     if constexpr (FILTER) {
       if ((((c0 - c_begin) / TW) & 3) == 3) advance_theta();
@@ -445,7 +461,8 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     tile(S0{}, c0);
     if (c0 + TW < c_end) tile(S1{}, c0 + TW);
   }
-  epilogue(1, prev_c0, key_prev, scale_prev, true);
+  partial(1, p1);
+  epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, true);
   if constexpr (FILTER) {
     if (l == 0 && t_first < r_end) a.ccount[(long long)b * a.n_rows + t_first - a.row0] = f_cnt;
   }
