@@ -60,28 +60,6 @@ __device__ __forceinline__ float fp8_to_f32(uint32_t code) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// LDS byte address of a pointer into workgroup memory.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land
-// at lds + BYTES * l (lds wave-uniform).  Written as inline assembly so that
-// the compiler does not pair every later LDS read with a wait for all
-// outstanding copies: the caller waits for them with s_waitcnt itself.  M0
-// (which holds the LDS base) is saved and restored; no VGPR is written.
-template <int BYTES>
-__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
-  uint32_t saved;
-  if constexpr (BYTES == 16)
-    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
-                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
-  else
-    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
-                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
-}
-
-
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, kWave); }
 
 // Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).

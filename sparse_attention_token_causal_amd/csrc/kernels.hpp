@@ -83,7 +83,7 @@ struct SelectArgs {
   int* out;               // [B * n_rows, topk], indexed by flattened row
 };
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int gather);
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter);
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st);

@@ -98,10 +98,6 @@ __device__ __forceinline__ int row_limit(const ScoreArgs& a, int r) {
   return mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, r);
 }
 
-// Waits until at most n vector-memory operations of this wave are in flight
-// and every LDS operation has completed (s_waitcnt vmcnt(n) lgkmcnt(0)).
-#define IDX_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70)
-
 // Scheduling groups for the instruction scheduler (gfx9 sched_group_barrier masks).
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
@@ -116,15 +112,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   constexpr int kScoreThreads = NWV * 64;  // threads of this workgroup
   typedef MfmaTraits<QF, KF> M;
   constexpr int NKS = D / M::KSTEP;
-  // bfloat16 keys scanned by position arrive by direct global -> LDS copies
-  // into unpadded rows whose 16-byte chunks are XOR-swizzled by row; the
-  // other variants stage through registers into rows padded by 16 bytes
-  constexpr bool DMA = QF == BF16 && KF == BF16 && !GATHER;
-  constexpr int ROWB = DMA ? D * M::KE : D * M::KE + 16;
-  constexpr int CK = D * M::KE / 16;  // 16-byte chunks per key row
-  // LDS key tiles: three with direct copies (a tile is fetched two tiles
-  // ahead), two with register staging
-  constexpr int NBUF = DMA ? 3 : 2;
+  constexpr int ROWB = D * M::KE + 16;
   constexpr int QW = 64 / H;                  // queries per wave
   constexpr int NW = NWV;                     // waves per workgroup
   constexpr int KW = NW / RW, TW = KW * 64;   // key-waves, tile width (columns)
@@ -198,7 +186,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   }
 
   // ---- filtering state (one query per wave; wave-uniform) ----
-  uint32_t* hist = (uint32_t*)(smem + NBUF * TILE_BYTES) + wave * kFiltBins;
+  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES) + wave * kFiltBins;
   int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0;
   float f_lo = neg_inf();  // lower edge of bin f_theta (-inf while f_theta == 0)
   bool f_based = false;
@@ -286,37 +274,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   auto load_block = [&](frag_t* bf, int buf, int cb) {
     const char* ldsrow = smem + buf * TILE_BYTES + (kw * 64 + cb * 32 + l32) * ROWB;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if constexpr (DMA)  // chunk 2 ks + half of the row, swizzled (row % CK = l32 % CK)
-        bf[ks] = *(const frag_t*)(ldsrow + 16 * ((2 * ks + half) ^ (l32 % CK)));
-      else
-        bf[ks] = M::load_b(ldsrow, ks, half);
-    }
-  };
-  // Direct copies of the TW keys from c0n into LDS buffer bufn: copy d fills
-  // bytes [1024 d, 1024 d + 1024) of the tile, lane l the 16 bytes at 16 l:
-  // key r = p / CK, chunk position cp = p % CK (p = 64 d + l), which holds
-  // the key's chunk cp ^ (r % CK), so that the fragment reads of eight
-  // consecutive keys hit distinct bank groups.  Columns past the range copy
-  // the range's last key (in bounds; masked in the epilogue).
-  constexpr int NDMA = TW * ROWB / 1024;  // 1 KiB copies per tile
-  constexpr int NDW = NDMA / NW;           // issued by each wave
-  static_assert(!DMA || NDMA % NW == 0, "every wave issues the same number of copies");
-  auto dma_issue = [&](int c0n, int bufn) {
-    if constexpr (DMA) {
-      char* kt = smem + bufn * TILE_BYTES;
-#pragma unroll
-      for (int d0 = 0; d0 < NDMA; d0 += NW) {
-        const int d = d0 + wave;
-        {
-          const int p = d * 64 + l;
-          const int r = p / CK, cp = p % CK;
-          const int col = min(c0n + r, c_end - 1);
-          copy_to_lds<16>(kseq + (size_t)col * ROWB + 16 * (cp ^ (r % CK)),
-                        __builtin_amdgcn_readfirstlane(lds_addr(kt + d * 1024)));
-        }
-      }
-    }
+    for (int ks = 0; ks < NKS; ++ks) bf[ks] = M::load_b(ldsrow, ks, half);
   };
   auto mfma_block = [&](const frag_t* bf, int buf, int cb) {
     if constexpr (PRELOAD) {
@@ -455,19 +413,9 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // set P holds the tiles of parity P between their load and their store).
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  if constexpr (DMA) {
-    dma_issue(c_begin, 0);
-    if (c_begin + TW < c_end) {
-      dma_issue(c_begin + TW, 1);
-      IDX_WAIT_VM_LDS(NDW);  // the first tile's copies (loads complete in order)
-    } else {
-      IDX_WAIT_VM_LDS(0);
-    }
-  } else {
-    stage_load(S0{}, c_begin);
-    if (c_begin + TW < c_end) stage_load(S1{}, c_begin + TW);
-    stage_store(S0{}, 0);
-  }
+  stage_load(S0{}, c_begin);
+  if (c_begin + TW < c_end) stage_load(S1{}, c_begin + TW);
+  stage_store(S0{}, 0);
   __syncthreads();
   int buf = 0, prev_c0 = c_begin, key_prev = -1;
   float scale_prev = 1.f;
@@ -479,9 +427,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     constexpr int PAR = decltype(par_c)::value;  // parity of this tile's index
     using Cur = std::integral_constant<int, PAR>;
     using Nxt = std::integral_constant<int, 1 - PAR>;
-    if constexpr (!DMA) {
-      if (c0 + 2 * TW < c_end) stage_load(Cur{}, c0 + 2 * TW);
-    }
+    if (c0 + 2 * TW < c_end) stage_load(Cur{}, c0 + 2 * TW);
     int key_cur = c0 + jl;
     float scale_cur = 1.f;
     if (COLINFO) {
@@ -504,28 +450,12 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     if constexpr (FILTER) {
       if ((((c0 - c_begin) / TW) & 3) == 3) advance_theta();
     }
-    if constexpr (!DMA) {
-      if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
-      __syncthreads();
-    } else {
-      // Copies of the tile after next go into the buffer the previous tile
-      // used (released by the barrier that ended it), as this wave's last
-      // vector-memory operations of the tile; loads and stores complete in
-      // order, so waiting until only those are outstanding means the next
-      // tile's copies (and every store) have landed.  Then the barrier.
-      if (c0 + 2 * TW < c_end) {
-        dma_issue(c0 + 2 * TW, buf == 0 ? 2 : buf - 1);
-        IDX_WAIT_VM_LDS(NDW);
-      } else {
-        IDX_WAIT_VM_LDS(0);
-      }
-      __builtin_amdgcn_s_barrier();
-      __asm__ __volatile__("" ::: "memory");
-    }
+    if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
+    __syncthreads();
     prev_c0 = c0;
     key_prev = key_cur;
     scale_prev = scale_cur;
-    buf = (buf + 1 == NBUF) ? 0 : buf + 1;
+    buf ^= 1;
   };
   for (int c0 = c_begin; c0 < c_end; c0 += 2 * TW) {
     tile(S0{}, c0);
@@ -538,7 +468,6 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   }
 #undef IDX_INTERLEAVE
 }
-#undef IDX_WAIT_VM_LDS
 
 template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER = false>
 static hipError_t launch_mode(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
@@ -590,21 +519,19 @@ static hipError_t pick_h(const ScoreArgs& a, int H, int D, dim3 grid, size_t lds
   return hipErrorInvalidValue;
 }
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int gather) {
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter) {
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
   const int tw = (nw / rw) * 64;
-  // bfloat16 keys by position: three unpadded tiles (direct copies);
-  // otherwise two tiles with 16-byte row padding; then one filtering
-  // histogram per wave
-  const bool dma = qf == BF16 && kf == BF16 && !gather;
-  return (dma ? 3 : 2) * ((size_t)tw * (D * ke + (dma ? 0 : 16)) + (size_t)tw * 8) +
+  (void)kf;
+  // double-buffered tiles, then one filtering histogram per wave
+  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) +
          (filter ? (size_t)nw * kFiltBins * 4 : 0);
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st) {
   dim3 grid(a.n_blocks, n_col_chunks);
-  const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter, a.mode == kModeGather);
+  const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter);
   if (qf == F32 && kf == F32) return pick_h<F32, F32>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == BF16) return pick_h<BF16, BF16>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == FP8) return pick_h<BF16, FP8>(a, H, D, grid, lds, st);

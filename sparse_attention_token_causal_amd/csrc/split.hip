@@ -48,6 +48,27 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
 // (s_waitcnt with the export and LDS counters left at their maxima).
 #define IDX_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
 
+// LDS byte address of a pointer into workgroup memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct global -> LDS copy of BYTES (4 or 16) per lane: lane l's bytes land
+// at lds + BYTES * l (lds wave-uniform).  Written as inline assembly so that
+// the compiler does not pair every later LDS read with a wait for all
+// outstanding copies: the caller waits for them with s_waitcnt itself.  M0
+// (which holds the LDS base) is saved and restored; no VGPR is written.
+template <int BYTES>
+__device__ __forceinline__ void copy_to_lds(const void* src, uint32_t lds) {
+  uint32_t saved;
+  if constexpr (BYTES == 16)
+    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, off\n\ts_mov_b32 m0, %0"
+                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
+  else
+    __asm__ __volatile__("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dword %2, off\n\ts_mov_b32 m0, %0"
+                         : "=&s"(saved) : "s"(lds), "v"(src) : "memory");
+}
+
 template <int QF, int KF, int H, int D, int RWN>
 __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
   constexpr bool F8MMA = (QF == FP8);          // fp8 x fp8 (keys are FP8 too)
