@@ -216,7 +216,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
       se.mode = kModeList;
       se.scores = flt.val;
       se.lidx = flt.idx;
-      se.counts = flt.count;
+      se.finfo = flt.count;
     }
     if (timed(IDX_KERNEL_SELECT, st, [&] { return launch_select(se, (int)(r1 - r0), st); }) != hipSuccess)
       return IDX_EHIP;
@@ -248,9 +248,10 @@ ScoreArgs base_args(const idx_problem* p) {
 bool use_filter(const idx_problem* p, const Layout& L) { return L.filter && p->heads == 64; }
 
 // Workspace bytes per buffered row of a dense scan: a float score row, or a
-// candidate list (float score + int key per slot) and its count.
+// candidate list (float score + int key per slot) and the scan's four-int
+// record for the select.
 size_t score_row_bytes(const idx_problem* p, const Layout& L) {
-  return use_filter(p, L) ? (size_t)p->n_k * 8 + 4 : (size_t)p->n_k * 4;
+  return use_filter(p, L) ? (size_t)p->n_k * 8 + 16 : (size_t)p->n_k * 4;
 }
 
 int proxy_q_dtype(const idx_problem* p) { return p->q_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
@@ -604,7 +605,7 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
   if (!use_filter(p, L))
     return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
                             (float*)ws, rows, false, topk, out_idx, st);
-  // layout: [rows, n_k] float scores, [rows, n_k] int keys, [rows] counts
+  // layout: [rows, n_k] float scores, [rows, n_k] int keys, [rows, 4] select records
   Filter flt;
   flt.on = true;
   flt.val = (float*)ws;

@@ -28,6 +28,16 @@ __host__ __device__ inline int mode_limit(int mode, int q_pos0, int n_q, int gro
   return q_pos0 + r;
 }
 
+// Per-row record a filtering scan leaves for the select: the number of
+// candidates, the histogram base (bin = clamp((order key >> 15) - base, 0,
+// 2047)), the boundary bin - the highest bin with at least topk candidates
+// at or above it (-2: fewer than topk candidates in all; -1: the boundary
+// bin holds more than kFiltBoundaryMax of them) - and the number of
+// candidates in bins above it.
+constexpr int kFiltBins = 2048;  // filter histogram: 256 bins per octave of the score, 8 octaves
+constexpr int kFiltInfoCount = 0, kFiltInfoBase = 1, kFiltInfoBoundary = 2, kFiltInfoAbove = 3;
+constexpr int kFiltBoundaryMax = 256;
+
 struct ScoreArgs {
   const void* q;          // [B, n_rows, H, D] rows (queries or proxies)
   const float* q_scale;   // [B, n_rows] (FP8 q only)
@@ -49,8 +59,9 @@ struct ScoreArgs {
   // Candidate filtering (dense scans with one query per wave, whole rows per
   // workgroup): instead of full score rows, each row's candidates - every key
   // whose score reaches the row's running threshold bin - are written as
-  // (score, key) pairs at cval/cidx + (row - row0) * cld and their number at
-  // ccount[row - row0].  `topk` sets the threshold.
+  // (score, key) pairs at cval/cidx + (row - row0) * cld, and at
+  // ccount + 4 (row - row0) the row's record for the select (see
+  // kFiltInfo*): `topk` sets the threshold.
   int filter;
   float* cval;
   int* cidx;
@@ -71,6 +82,9 @@ struct SelectArgs {
   const int* cand;        // gather: key index of each column
   const int* lidx;        // list: key indices, same layout as scores
   const int* counts;      // list: entries per launch row
+  // filtered lists (when finfo is set; counts is then unused): launch row i's
+  // record finfo[4 i + kFiltInfo*] from the filtering scan
+  const int* finfo;
   // segmented list (when seg_counts is set; counts is then unused): launch
   // row i holds seg_counts[i * n_segs + s] entries of segment s at
   // scores/lidx + i * ld + s * seg_len; they are gathered into gval/gidx

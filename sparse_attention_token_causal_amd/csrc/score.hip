@@ -105,7 +105,6 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // columns are key positions (dense scan, proxy scan).
 // Filtering: bins of the running per-row histogram (256 per octave of the
 // score, a window of 8 octaves placed from the first tile's largest score).
-constexpr int kFiltBins = 2048;
 
 template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER>
 __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
@@ -464,7 +463,31 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   partial(1, p1);
   epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, true);
   if constexpr (FILTER) {
-    if (l == 0 && t_first < r_end) a.ccount[(long long)b * a.n_rows + t_first - a.row0] = f_cnt;
+    // The histogram counts every written candidate in its bin, so the bin
+    // where the count from the top reaches topk (and the count above it)
+    // is exact: the select then only ranks that bin's candidates.
+    int above = 0, bstar = -2, cnt_b = 0;
+    for (int hi = kFiltBins; hi > 0; hi -= kWave) {
+      const int h = (int)hist[hi - 1 - l];  // lane j: bin hi - 1 - j (from the top)
+      const int incl = wave_incl_scan(h);
+      const unsigned long long m = __ballot(above + incl >= a.topk);
+      if (m) {
+        const int J = __builtin_ctzll(m);
+        const int hJ = __shfl(h, J, kWave), iJ = __shfl(incl, J, kWave);
+        bstar = hi - 1 - J;
+        cnt_b = hJ;
+        above += iJ - hJ;
+        break;
+      }
+      above += __shfl(incl, kWave - 1, kWave);
+    }
+    if (l == 0 && t_first < r_end) {
+      int* info = a.ccount + 4 * ((long long)b * a.n_rows + t_first - a.row0);
+      info[kFiltInfoCount] = f_cnt;
+      info[kFiltInfoBase] = f_base;
+      info[kFiltInfoBoundary] = (bstar == -2 || cnt_b <= kFiltBoundaryMax) ? bstar : -1;
+      info[kFiltInfoAbove] = above;
+    }
   }
 #undef IDX_INTERLEAVE
 }

@@ -50,7 +50,8 @@ struct SelectShared {
 };
 
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
-  if (a.mode == kModeList) return min(a.counts[blockIdx.x], a.n_cols);
+  if (a.mode == kModeList)
+    return min(a.finfo ? a.finfo[4 * (long long)blockIdx.x + kFiltInfoCount] : a.counts[blockIdx.x], a.n_cols);
   if (a.mode == kModeGather) return a.n_cols;
   const int lim = mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, r);
   return min(lim + 1, a.n_cols);
@@ -100,6 +101,73 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   }
   if (a.mode == kModeList) crow = a.lidx + (long long)blockIdx.x * a.ld;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+  if (a.mode == kModeList && a.finfo) {
+    // A filtered list with its scan's record: one pass writes every
+    // candidate above the boundary bin (there are exactly `above` of them),
+    // collects the boundary bin's candidates (at most kFiltBoundaryMax), and
+    // those are ranked exactly by (score descending, key ascending).
+    const int* fi = a.finfo + 4 * (long long)blockIdx.x;
+    const int bstar = fi[kFiltInfoBoundary];
+    if (bstar != -1) {
+      const int n = min(fi[kFiltInfoCount], a.n_cols), base = fi[kFiltInfoBase];
+      const bool all = bstar == -2;  // fewer than topk candidates: all of them
+      const int above = all ? n : fi[kFiltInfoAbove];
+      if (tid == 0) sh.list_n = 0;
+      __syncthreads();
+      int wbase = 0;
+      for (int c0 = 0; c0 < n; c0 += 8 * NT) {
+        uint32_t k[8];
+        int x[8], win = 0;
+        bool bnd[8], wn[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = min(c0 + j * NT + tid, n - 1);
+          k[j] = order_key(row[c]);
+          x[j] = crow[c];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool in = c0 + j * NT + tid < n;
+          const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
+          wn[j] = in && (all || bin > bstar);
+          bnd[j] = in && !all && bin == bstar;
+          win += wn[j] ? 1 : 0;
+        }
+        int tot;
+        int pos = wbase + block_excl_scan<NT>(win, &tot, sh);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (wn[j]) {
+            if (pos < a.topk) out[pos] = x[j];
+            ++pos;
+          }
+          if (bnd[j]) {
+            const int p = atomicAdd(&sh.list_n, 1);
+            if (p < kListCap) {
+              sh.lkey[p] = k[j];
+              sh.lidx[p] = x[j];
+            }
+          }
+        }
+        wbase += tot;
+      }
+      __syncthreads();
+      const int m = min(sh.list_n, kListCap), need = all ? 0 : a.topk - above;
+      for (int e = tid; e < m; e += NT) {
+        const uint32_t ke = sh.lkey[e];
+        const int ie = sh.lidx[e];
+        int rank = 0;
+        for (int f = 0; f < m; ++f) {
+          const uint32_t kf = sh.lkey[f];
+          rank += (kf > ke || (kf == ke && sh.lidx[f] < ie)) ? 1 : 0;
+        }
+        if (rank < need) out[above + rank] = ie;
+      }
+      const int filled = min(a.topk, all ? n : above + min(need, m));
+      for (int i = filled + tid; i < a.topk; i += NT) out[i] = -1;
+      return;
+    }
+  }
   int len;
   if (a.mode == kModeList && a.seg_counts) {
     // Segmented list: segment s of the row holds seg_counts[s] entries from
@@ -451,8 +519,10 @@ static hipError_t launch_by_length(const SelectArgs& a, int rows, int n, hipStre
 // sequence; such launches are split into length classes so that each class
 // runs the smallest variant that holds its rows.
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st) {
-  // candidate lists are mostly short; a longer list streams inside the kernel
-  if (a.mode == kModeList) return launch_kpt<512, 16>(a, n_launch_rows, st);
+  // candidate lists (up to a few k (1 + ln(n / k)) entries) are held 32 keys
+  // per thread by 256-thread workgroups, more rows in flight per CU than
+  // with 512 threads; a longer list streams inside the kernel
+  if (a.mode == kModeList) return launch_kpt<256, 32>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
   const int classes[4] = {256 * 8, 512 * 16, 1024 * 16, 1024 * 32};
   long long r = 0;

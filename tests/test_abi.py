@@ -172,11 +172,11 @@ def test_workspace_sizes_follow_the_layout(lib):
     need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 8)
     assert need >= 1000 * 1000 * 4 and need % 256 == 0
     # large: about 1 GiB-worth of buffered score rows; with 64 heads the rows
-    # are candidate lists (score + key per slot, plus a count): twice that
+    # are candidate lists (score + key per slot, plus a 16-byte record): twice that
     big = problem(n_q=131072, n_k=131072)
     nb = lib.idx_workspace_bytes(ctypes.byref(big), 0, 0, 0, 2048)
     rows = (1 << 30) // (131072 * 4)
-    assert nb >= rows * (131072 * 8 + 4) and nb <= (rows + 8) * (131072 * 8 + 4) + 256
+    assert nb >= rows * (131072 * 8 + 16) and nb <= (rows + 8) * (131072 * 8 + 16) + 256
     big32 = problem(n_q=131072, n_k=131072, heads=32)
     nb32 = lib.idx_workspace_bytes(ctypes.byref(big32), 0, 0, 0, 2048)
     assert (1 << 30) <= nb32 <= (1 << 30) + 16 * 131072 * 4 + 256

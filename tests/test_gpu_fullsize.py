@@ -81,7 +81,7 @@ def test_prefill_bf16_L32768():
     # the timed configuration: one workspace for every row (candidate filtering)
     p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
     ws = torch.empty(max(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk),
-                         wl.n_q * (wl.n_k * 8 + 4) + 4096), dtype=torch.uint8, device=dev)
+                         wl.n_q * (wl.n_k * 8 + 16) + 4096), dtype=torch.uint8, device=dev)
     idx = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, workspace=ws, **a)
     torch.cuda.synchronize()
     del ws
