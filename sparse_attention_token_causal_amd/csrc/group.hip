@@ -15,36 +15,73 @@ namespace idx {
 // order in float32, then divide by the member count; the proxy q is stored
 // as bfloat16 (nearest, ties to even) for BF16/FP8 inputs and as float32 for
 // F32 inputs, the proxy w as float32.  HBM-bound: every q element is read
-// once, coalesced along (head, dim).
+// once; each thread owns 16-byte chunks of the (head, dim) row (coalesced
+// across the workgroup) and keeps four members' loads in flight.
 template <int QF>
 __global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const float* q_scale,
                                                           const float* w, int n_q, int H, int D,
                                                           int group, void* pq, float* pw) {
+  constexpr int EB = QF == F32 ? 4 : (QF == BF16 ? 2 : 1);  // bytes per q element
+  constexpr int VEC = 16 / EB;                              // elements per 16-byte chunk
   const int g = blockIdx.x, b = blockIdx.y;
   const int n_g = (n_q + group - 1) / group;
   const int t0 = g * group, t1 = min(t0 + group, n_q);
   const float n = (float)(t1 - t0);
   const size_t HD = (size_t)H * D;
   const size_t prow = (size_t)b * n_g + g;
-  for (size_t e = threadIdx.x; e < HD; e += blockDim.x) {
-    float s = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      const size_t off = ((size_t)b * n_q + t) * HD + e;
-      float v;
-      if (QF == F32) {
-        v = ((const float*)q)[off];
-      } else if (QF == BF16) {
-        v = __uint_as_float((uint32_t)((const uint16_t*)q)[off] << 16);
-      } else {
-        v = fp8_to_f32(((const uint8_t*)q)[off]) * q_scale[(size_t)b * n_q + t];
+  const char* qb = (const char*)q + (size_t)b * n_q * HD * EB;
+  auto decode = [&](const i32x4& raw, int t, float* v) {
+    if constexpr (QF == F32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = __int_as_float(raw[i]);
+    } else if constexpr (QF == BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float((uint32_t)raw[i] << 16);
+        v[2 * i + 1] = __uint_as_float((uint32_t)raw[i] & 0xFFFF0000u);
       }
-      s += v;
+    } else {
+      const float sc = q_scale[(size_t)b * n_q + t];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = fp8_to_f32(((uint32_t)raw[i / 4] >> (8 * (i % 4))) & 0xFFu) * sc;
     }
-    const float m = s / n;
-    if (QF == F32)
-      ((float*)pq)[prow * HD + e] = m;
-    else
-      ((uint16_t*)pq)[prow * HD + e] = f32_to_bf16_rne(m);
+  };
+  for (size_t ch = threadIdx.x; ch * VEC < HD; ch += blockDim.x) {
+    float s[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) s[i] = 0.f;
+    int t = t0;
+    for (; t + 4 <= t1; t += 4) {
+      i32x4 raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = *(const i32x4*)(qb + ((size_t)(t + u) * HD + ch * VEC) * EB);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float v[VEC];
+        decode(raw[u], t + u, v);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) s[i] += v[i];
+      }
+    }
+    for (; t < t1; ++t) {
+      float v[VEC];
+      decode(*(const i32x4*)(qb + ((size_t)t * HD + ch * VEC) * EB), t, v);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s[i] += v[i];
+    }
+    const size_t o = prow * HD + ch * VEC;
+    if constexpr (QF == F32) {
+      *(float4*)((float*)pq + o) = make_float4(s[0] / n, s[1] / n, s[2] / n, s[3] / n);
+    } else {
+      uint32_t packed[VEC / 2];
+#pragma unroll
+      for (int i = 0; i < VEC / 2; ++i)
+        packed[i] = (uint32_t)f32_to_bf16_rne(s[2 * i] / n) | ((uint32_t)f32_to_bf16_rne(s[2 * i + 1] / n) << 16);
+#pragma unroll
+      for (int i = 0; i < VEC / 8; ++i)
+        *(i32x4*)((uint16_t*)pq + o + 8 * i) =
+            i32x4{(int)packed[4 * i], (int)packed[4 * i + 1], (int)packed[4 * i + 2], (int)packed[4 * i + 3]};
+    }
   }
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
     float s = 0.f;
