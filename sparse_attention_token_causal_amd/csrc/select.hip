@@ -507,9 +507,11 @@ static hipError_t launch_kpt(const SelectArgs& a, int rows, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Smallest variant that holds a row of n keys in registers; up to 8192 keys
+// 256-thread workgroups (more rows in flight per CU than wider ones).
 static hipError_t launch_by_length(const SelectArgs& a, int rows, int n, hipStream_t st) {
   if (n <= 256 * 8) return launch_kpt<256, 8>(a, rows, st);
-  if (n <= 512 * 16) return launch_kpt<512, 16>(a, rows, st);
+  if (n <= 256 * 32) return launch_kpt<256, 32>(a, rows, st);
   if (n <= 1024 * 16) return launch_kpt<1024, 16>(a, rows, st);
   if (n <= 1024 * 32) return launch_kpt<1024, 32>(a, rows, st);
   return launch_kpt<1024, 0>(a, rows, st);
@@ -524,7 +526,7 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
   // with 512 threads; a longer list streams inside the kernel
   if (a.mode == kModeList) return launch_kpt<256, 32>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
-  const int classes[4] = {256 * 8, 512 * 16, 1024 * 16, 1024 * 32};
+  const int classes[4] = {256 * 8, 256 * 32, 1024 * 16, 1024 * 32};
   long long r = 0;
   while (r < n_launch_rows) {
     // the length of launch row r, and the longest run of rows in its class
