@@ -13,11 +13,13 @@
 //    (query, head) rows - at most 4 queries, 256 rows - are split into
 //    64-row waves whose q fragments stay in registers, and the other waves
 //    of the workgroup take alternate 32-column steps of the chunk;
-//  * no LDS staging: each lane loads the half key row of its own MFMA
-//    column straight into registers.  The head dimension is permuted (the
-//    same way for q and k, which leaves every dot product unchanged) so that
-//    lane half h covers the contiguous half [h*d/2, (h+1)*d/2) of the row;
-//    a ring of P steps keeps several loads per wave in flight;
+//  * the key rows of each 32-column step are copied straight from global
+//    memory into an LDS ring of P steps (direct-to-LDS loads, no register
+//    staging, several steps in flight); the row-waves of a column group
+//    share them, and each lane then reads the half key row of its own MFMA
+//    column.  The head dimension is permuted (the same way for q and k,
+//    which leaves every dot product unchanged) so that lane half h covers
+//    the contiguous half [h*d/2, (h+1)*d/2) of the row;
 //  * FP8 keys under bfloat16 q are widened to bfloat16 in registers (exact);
 //    FP8 x FP8 runs the f8f6f4 MFMA directly;
 //  * the epilogue is the tiled scan's: ReLU, x w (x q scale), head sum in
@@ -215,6 +217,12 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
   };
 
+  // last visible key of each of this wave's queries (-1 past the row set)
+  int qlim[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi)
+    qlim[qi] = t_first + qi < a.n_rows ? mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, t_first + qi) : -1;
+
   // ---- epilogue of step i: ReLU, x w, head sum, key scale, mask -> LDS scores + histogram ----
   auto epilogue = [&](const f32x16* acc, int i, float ksc) {
     const int col_raw = c_begin + 32 * (cw + CWN * i) + l32;
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       // of the chunk's last column and stores it there again (same value).
       // Only half (qi % 2)'s lanes inside the chunk count.
       if (QW == 1 || t < a.n_rows) {
-        const bool ok = col <= mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, t);
+        const bool ok = col <= qlim[qi];
         const float val = ok ? (KF == FP8 ? tot * ksc : tot) : neg_inf();
         ssc[t * a.kc + (col - c_begin)] = val;
         const uint32_t bin = order_key(val) >> kSplitShift;
@@ -422,6 +430,7 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
 
   // thread i owns bins [16 i, 16 i + 16): the threshold is the highest bin
   // with at least `need` counts at or above it (0 when the sum falls short)
+  static_assert(kSplitBins == 16 * 256, "16 bins per thread of the 256");
   uint32_t c[16];
   int mine = 0;
 #pragma unroll
