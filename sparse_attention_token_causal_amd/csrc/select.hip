@@ -85,8 +85,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, SelectShared& 
 // NT threads per row.  KPT > 0: each thread keeps the keys of columns
 // tid + i*NT (i < KPT) in registers.  KPT == 0: rows of any length, re-read
 // from global memory in batches of 8 loads per thread.
+// A row's select is a chain of short dependent phases (loads, reductions,
+// histogram, scans), so rows in flight per CU decide its speed: 256-thread
+// workgroups are held to at least four waves per SIMD (at most 128 VGPRs,
+// four rows per CU; the LDS would allow five).
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArgs a) {
   constexpr int kSelectThreads = NT;
   constexpr int kNW = NT / kWave;
   __shared__ SelectShared sh;
