@@ -62,21 +62,24 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, kWave); }
 
-// Wave-wide inclusive prefix sum of an int (Hillis-Steele over 64 lanes).
+// Wave-wide inclusive prefix sum of an int on DPP lane moves (VALU, no LDS
+// round trips): shifts by 1, 2, 4 and 8 inside each row of 16 lanes (a lane
+// without a source adds 0), then row 0's total into row 1 and row 2's into
+// row 3 (row_bcast:15), then the total of rows 0-1 into rows 2-3
+// (row_bcast:31).  Every lane must be active.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    int o = __shfl_up(v, off, kWave);
-    if (l >= off) v += o;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
+// Wave-wide sum (every lane active), returned wave-uniform.
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);
 }
 
 }  // namespace idx

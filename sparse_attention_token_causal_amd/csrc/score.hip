@@ -385,7 +385,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // Raise the threshold bin: advance over the lowest bins at or above it while
   // at least topk counted scores remain above them.  One gather of 64 bins,
   // a wave prefix sum and a ballot move it up to 64 bins at a time.  Called
-  // every few tiles: a stale threshold only admits extra candidates.
+  // every eight tiles: a stale threshold only admits extra candidates, and
+  // each call is a chain of dependent LDS and cross-lane steps that the
+  // wave cannot overlap with its MFMAs (every four tiles cost about 3% more
+  // scan time than every eight, every sixteen about the same).
   auto advance_theta = [&]() {
     for (;;) {
       const int bi = f_theta + l;
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     partial(0, p0_prev);
     IDX_INTERLEAVE(1, false);
     if constexpr (FILTER) {
-      if ((((c0 - c_begin) / TW) & 3) == 3) advance_theta();
+      if ((((c0 - c_begin) / TW) & 7) == 7) advance_theta();
     }
     if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
     __syncthreads();
