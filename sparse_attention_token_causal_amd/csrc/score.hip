@@ -429,7 +429,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     constexpr int PAR = decltype(par_c)::value;  // parity of this tile's index
     using Cur = std::integral_constant<int, PAR>;
     using Nxt = std::integral_constant<int, 1 - PAR>;
-    if (c0 + 2 * TW < c_end) stage_load(Cur{}, c0 + 2 * TW);
+    // unconditional (addresses clamped into the range): the compiler then
+    // counts these loads on every path and waits only for the older set
+    // before storing it, instead of for every load in flight
+    stage_load(Cur{}, c0 + 2 * TW);
     int key_cur = c0 + jl;
     float scale_cur = 1.f;
     if (COLINFO) {
