@@ -179,6 +179,8 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     }
     int kc = ceil_div(L.n_cols, chunks);
     kc = ceil_div(kc, tw) * tw;
+    // a gather workgroup stages its columns' key indices in LDS
+    if (L.mode == kModeGather && kc > kCandLdsMax) kc = kCandLdsMax;
     chunks = ceil_div(L.n_cols, kc);
     sa.blk0 = blk0;
     sa.n_blocks = nb;

@@ -47,7 +47,9 @@ struct ScoreArgs {
   int n_rows, n_k, n_q, q_pos0, group;
   int block;              // key-block size (kModeBlock)
   int n_cols;             // n_k (dense, proxy) or n_cand (gather)
-  const int* cand;        // [B, n_g, n_cand] (gather only)
+  // [B, n_g, n_cand] (gather only).  A gather workgroup first copies the key
+  // indices of its columns [c, c + kc) into LDS (kc <= kCandLdsMax).
+  const int* cand;
   int mode;
   int blk0, n_blocks;     // block ids [blk0, blk0 + n_blocks) in this launch
   long long row0;         // flattened row (b * n_rows + r) stored at out row 0
@@ -97,7 +99,9 @@ struct SelectArgs {
   int* out;               // [B * n_rows, topk], indexed by flattened row
 };
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter);
+// Candidate columns one gather workgroup takes (their key indices are staged in LDS).
+constexpr int kCandLdsMax = 16384;
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int gather_cols);
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st);
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st);

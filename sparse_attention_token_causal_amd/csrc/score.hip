@@ -198,8 +198,15 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     f_idx = a.cidx + crow * a.cld;
   }
 
-  const int* cand_row = nullptr;
-  if (GATHER) cand_row = a.cand + ((size_t)b * ((a.n_q + a.group - 1) / a.group) + g) * a.n_cols;
+  // Gathered columns: the workgroup's candidate key indices are copied to
+  // LDS once (after the tile buffers), so staging a key tile reads them from
+  // LDS instead of issuing global loads that the key-row loads depend on.
+  int* s_cand = (int*)(smem + 2 * TILE_BYTES);
+  if constexpr (GATHER) {
+    const int* cand_row = a.cand + ((size_t)b * ((a.n_q + a.group - 1) / a.group) + g) * a.n_cols;
+    for (int i = threadIdx.x; i < c_end - c_begin; i += kScoreThreads) s_cand[i] = cand_row[c_begin + i];
+    __syncthreads();
+  }
   const char* kseq = (const char*)a.k + (size_t)b * a.n_k * D * M::GE;
 
   // ---- staging of one key tile: global -> registers -> LDS (double buffered) ----
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       const int col = min(c0 + j, c_end - 1);
       int s, srow;
       if (GATHER) {
-        s = cand_row[col];
+        s = s_cand[col - c_begin];
         if (c0 + j >= c_end || s >= a.n_k) s = -1;
         srow = s < 0 ? 0 : s;
       } else {
@@ -548,19 +555,21 @@ static hipError_t pick_h(const ScoreArgs& a, int H, int D, dim3 grid, size_t lds
   return hipErrorInvalidValue;
 }
 
-size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter) {
+size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int gather_cols) {
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
   const int tw = (nw / rw) * 64;
   (void)kf;
-  // double-buffered tiles, then one filtering histogram per wave
+  // double-buffered tiles, then one filtering histogram per wave (dense
+  // scans) or the workgroup's candidate key indices (gather)
   return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) +
-         (filter ? (size_t)nw * kFiltBins * 4 : 0);
+         (filter ? (size_t)nw * kFiltBins * 4 : 0) + (size_t)gather_cols * 4;
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st) {
   dim3 grid(a.n_blocks, n_col_chunks);
-  const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter);
+  if (a.mode == kModeGather && a.kc > kCandLdsMax) return hipErrorInvalidValue;
+  const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter, a.mode == kModeGather ? a.kc : 0);
   if (qf == F32 && kf == F32) return pick_h<F32, F32>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == BF16) return pick_h<BF16, BF16>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == FP8) return pick_h<BF16, FP8>(a, H, D, grid, lds, st);
