@@ -133,7 +133,8 @@ constexpr int split_ring_steps(int key_bytes, int d, int rwn) {
   return p > 16 ? 16 : p;
 }
 // LDS bytes of a split-scan workgroup: ring, per-wave key-scale rings (FP8
-// keys), chunk scores, 16-bit-packed histograms, head weights.
+// keys), chunk scores, 16-bit-packed histograms, each row's top counted bin
+// (within a final 1 KiB).
 constexpr size_t split_lds_bytes(int key_bytes, int d, int rwn, int n_rows, int kc) {
   return (size_t)(4 / rwn) * split_ring_steps(key_bytes, d, rwn) * split_step_bytes(key_bytes, d) +
          (key_bytes == 1 ? (size_t)4 * split_ring_steps(key_bytes, d, rwn) * 256 : 0) +

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
 
   // LDS: key ring [CWN][P][SB] | key-scale rings [4 waves][P][64] (FP8) |
   // chunk scores [n_rows][kc] | histograms [n_rows][kSplitBins / 2] (two
-  // 16-bit counters per word)
+  // 16-bit counters per word) | top counted bin [n_rows]
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* ring = smem;
   float* sscale = (float*)(ring + CWN * P * SB);
@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
     return;
   }
   for (int i = threadIdx.x; i < a.n_rows * (kSplitBins / 2); i += 256) shist[i] = 0u;
+  int* s_top = (int*)(shist + a.n_rows * (kSplitBins / 2));  // each row's top counted bin
+  if (threadIdx.x < a.n_rows) s_top[threadIdx.x] = -1;
 
   // ---- resident q fragments and head weights of this wave's 64 rows ----
   // (lane half h holds the elements [h d/2, (h+1) d/2) of each row: the d
@@ -152,7 +154,8 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
       if (t_first + ri / H >= a.n_rows) wreg[rb][v] = 0.f;
     }
   }
-  __syncthreads();  // histograms zeroed, q loads done
+  // (the histograms' zeroing and the q loads are complete at the barrier
+  // after the ring's first copies, so both latencies overlap)
 
   // ---- steps: group cw takes steps c_begin + 32 * (cw + CWN * i) ----
   const int n_steps = (c_end - c_begin + 31) / 32;
@@ -223,6 +226,11 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
   for (int qi = 0; qi < QW; ++qi)
     qlim[qi] = t_first + qi < a.n_rows ? mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, t_first + qi) : -1;
 
+  // each lane's highest counted bin per row (the row's histogram window ends
+  // at the maximum over the workgroup: no scan of the histogram at the end)
+  int topb[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) topb[qi] = -1;
   // ---- epilogue of step i: ReLU, x w, head sum, key scale, mask -> LDS scores + histogram ----
   auto epilogue = [&](const f32x16* acc, int i, float ksc) {
     const int col_raw = c_begin + 32 * (cw + CWN * i) + l32;
@@ -258,6 +266,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
         const uint32_t bin = order_key(val) >> kSplitShift;
         const bool count = ok && half == (qi & 1) && col_raw < c_end;
         atomicAdd(&shist[t * (kSplitBins / 2) + (bin >> 1)], count ? (1u << (16 * (bin & 1))) : 0u);
+        topb[qi] = count ? max(topb[qi], (int)bin) : topb[qi];
       }
     }
   };
@@ -313,6 +322,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
   };
   for (int i = 0; i < P - 1; ++i) issue(i);
   wait_step(std::integral_constant<int, P - 2>{});  // step 0 landed
+  __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): histograms zeroed
   __builtin_amdgcn_s_barrier();
   __asm__ __volatile__("" ::: "memory");
   if (has_rows) {
@@ -332,6 +342,15 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
     else
       epilogue(acc[0], n_iter - 1, ksc[0]);
   }
+  if (has_rows) {
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      int m = topb[qi];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+      if (l == 0 && t_first + qi < a.n_rows) atomicMax(&s_top[t_first + qi], m);
+    }
+  }
   IDX_WAIT_VM(0);   // the copies issued past the last step have landed too
   __syncthreads();  // every score and count in LDS
 
@@ -345,14 +364,7 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
   // ---- report each row's histogram window: the kSplitWin bins up to its top non-empty one ----
   for (int t = wave; t < a.n_rows; t += 4) {
     const uint32_t* hr = shist + t * (kSplitBins / 2);
-    int m = -1;
-#pragma unroll 16
-    for (int i = l; i < kSplitBins / 2; i += kWave) {
-      const uint32_t x = hr[i];
-      if (x) m = 2 * i + ((x >> 16) ? 1 : 0);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, kWave));
+    const int m = s_top[t];
     const int wb = m < 0 ? -1 : max(m - kSplitWin + 1, 0);
     const size_t slot = ((size_t)b * a.n_rows + t) * a.n_chunks + blockIdx.x;
     if (l == 0) a.wbase[slot] = wb;
