@@ -42,6 +42,7 @@ struct SelectShared {
   int wred[3][kMaxNW];
   int wscan[kMaxNW];
   int list_n;
+  int seg_max;  // segmented list: the largest segment count
   uint32_t sel_bin;
   int sel_above;
   // fallback radix state
@@ -188,20 +189,31 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
     }
   }
   int len;
+  constexpr int REG = KPT > 0 ? KPT : 1;
+  bool seg_direct = false;
   if (a.mode == kModeList && a.seg_counts) {
     // Segmented list: segment s of the row holds seg_counts[s] entries from
-    // position s * seg_len.  Gather them, in segment order, into one
-    // contiguous list (gval/gidx) that the rest of the kernel reads.
+    // position s * seg_len.  When every segment fits its threads' registers
+    // they are loaded from there directly (below); otherwise they are
+    // gathered, in segment order, into one contiguous list (gval/gidx) that
+    // the rest of the kernel reads.
     const int ns = a.n_segs;
     int tot;
+    if (tid == 0) sh.seg_max = 0;
     const int cnt = tid < ns ? a.seg_counts[(long long)blockIdx.x * ns + tid] : 0;
     const int ex = block_excl_scan<NT>(cnt, &tot, sh);
-    if (tid < ns) sh.soff[tid] = ex;
+    if (tid < ns) {
+      sh.soff[tid] = ex;
+      atomicMax(&sh.seg_max, cnt);
+    }
     if (tid == 0) sh.soff[ns] = tot;
     __syncthreads();
+    // Direct path: NT / ns threads per segment, each holding up to KPT of its
+    // segment's entries in registers (the order of a list is immaterial).
+    seg_direct = KPT > 0 && ns <= NT && sh.seg_max <= (NT / ns) * REG;
     float* gv = a.gval + (long long)blockIdx.x * a.ld;
     int* gi = a.gidx + (long long)blockIdx.x * a.ld;
-    for (int c0 = 0; c0 < tot; c0 += 8 * NT) {
+    for (int c0 = 0; c0 < (seg_direct ? 0 : tot); c0 += 8 * NT) {
       float v[8];
       int x[8];
 #pragma unroll
@@ -226,13 +238,14 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
       }
     }
     __syncthreads();
-    row = gv;
-    crow = gi;
+    if (!seg_direct) {
+      row = gv;
+      crow = gi;
+    }
     len = min(tot, a.n_cols);
   } else {
     len = row_length(a, r);
   }
-  constexpr int REG = KPT > 0 ? KPT : 1;
   uint32_t keys[REG];
   // rows longer than the register tile (possible for candidate lists) stream
   const bool regs = KPT > 0 && len <= REG * kSelectThreads;
@@ -276,16 +289,32 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   if (KPT > 0 && regs) {
     // every load of the row at once (clamped addresses: no per-element branch)
     float v[REG];
+    if (seg_direct) {
+      const int ns = a.n_segs, tps = NT / ns;
+      const int s = tid / tps, j0 = tid % tps;
+      const int cs = s < ns ? sh.soff[s + 1] - sh.soff[s] : 0;
 #pragma unroll
-    for (int i = 0; i < REG; ++i) {
-      const int cc = min(i * kSelectThreads + tid, max(len - 1, 0));
-      v[i] = row[cc];
-      if (indexed) idxs[i] = crow[cc];
-    }
+      for (int i = 0; i < REG; ++i) {
+        const int j = j0 + tps * i;
+        const long long cc = j < cs ? (long long)s * a.seg_len + j : 0;
+        v[i] = row[cc];
+        idxs[i] = crow[cc];
+      }
 #pragma unroll
-    for (int i = 0; i < REG; ++i) {
-      const int c = i * kSelectThreads + tid;
-      keys[i] = (c < len && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
+      for (int i = 0; i < REG; ++i)
+        keys[i] = (j0 + tps * i < cs && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
+    } else {
+#pragma unroll
+      for (int i = 0; i < REG; ++i) {
+        const int cc = min(i * kSelectThreads + tid, max(len - 1, 0));
+        v[i] = row[cc];
+        if (indexed) idxs[i] = crow[cc];
+      }
+#pragma unroll
+      for (int i = 0; i < REG; ++i) {
+        const int c = i * kSelectThreads + tid;
+        keys[i] = (c < len && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
+      }
     }
   }
   for_keys([&](int, uint32_t k, int) {

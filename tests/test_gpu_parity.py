@@ -55,6 +55,11 @@ DENSE = [
              seed=17, w_dist="int"),
     Workload("split_fp8_nq4_H16_d64_k2000", 1, 4, 2500, 16, 64, "fp8", "fp8", "normal8", "normal8",
              topk=2000, seed=18),
+    # every score of a query ties: every key of the prefix is a candidate, so
+    # the list segments overflow their threads' registers and the list select
+    # takes its gathering path (the other split cases load segments directly)
+    Workload("split_ties_const_keys_nq2_n20000_k300", 1, 2, 20000, 64, 128, "bf16", "bf16", "normal8", "const",
+             topk=300, seed=19),
 ]
 
 
