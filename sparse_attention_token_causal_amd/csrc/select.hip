@@ -42,7 +42,6 @@ struct SelectShared {
   int wred[3][kMaxNW];
   int wscan[kMaxNW];
   int list_n;
-  int seg_max;  // segmented list: the largest segment count
   uint32_t sel_bin;
   int sel_above;
   // fallback radix state
@@ -100,13 +99,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, SelectShared& 
 
 // NT threads per row.  KPT > 0: each thread keeps the keys of columns
 // tid + i*NT (i < KPT) in registers.  KPT == 0: rows of any length, re-read
-// from global memory in batches of 8 loads per thread.
+// from global memory in batches of 8 loads per thread.  SEGD: segmented
+// lists whose segments each fit their share of the threads' registers are
+// loaded from the segments directly (the decode lists' variant only: in the
+// others the extra path moves the register allocation of gathered rows into
+// spills).
 // A row's select is a chain of short dependent phases (loads, reductions,
 // histogram, scans), so rows in flight per CU decide its speed: 256-thread
 // workgroups are held to at least four waves per SIMD (at most 128 VGPRs,
 // four rows per CU; the LDS would allow five).
-template <int NT, int KPT>
+template <int NT, int KPT, bool SEGD = false>
 __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArgs a) {
+  static_assert(!SEGD || KPT > 0, "direct segment loads fill registers");
   constexpr int kSelectThreads = NT;
   constexpr int kNW = NT / kWave;
   __shared__ SelectShared sh;
@@ -189,28 +193,23 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
     }
   }
   int len;
-  constexpr int REG = KPT > 0 ? KPT : 1;
   bool seg_direct = false;
   if (a.mode == kModeList && a.seg_counts) {
     // Segmented list: segment s of the row holds seg_counts[s] entries from
-    // position s * seg_len.  When every segment fits its threads' registers
-    // they are loaded from there directly (below); otherwise they are
-    // gathered, in segment order, into one contiguous list (gval/gidx) that
-    // the rest of the kernel reads.
+    // position s * seg_len.  Gather them, in segment order, into one
+    // contiguous list (gval/gidx) that the rest of the kernel reads.
     const int ns = a.n_segs;
     int tot;
-    if (tid == 0) sh.seg_max = 0;
+    if (SEGD && tid == 0) sh.list_n = 0;  // (SEGD: the largest segment count until the list gather)
     const int cnt = tid < ns ? a.seg_counts[(long long)blockIdx.x * ns + tid] : 0;
     const int ex = block_excl_scan<NT>(cnt, &tot, sh);
-    if (tid < ns) {
-      sh.soff[tid] = ex;
-      atomicMax(&sh.seg_max, cnt);
-    }
+    if (tid < ns) sh.soff[tid] = ex;
+    if (SEGD && tid < ns) atomicMax(&sh.list_n, cnt);
     if (tid == 0) sh.soff[ns] = tot;
     __syncthreads();
-    // Direct path: NT / ns threads per segment, each holding up to KPT of its
-    // segment's entries in registers (the order of a list is immaterial).
-    seg_direct = KPT > 0 && ns <= NT && sh.seg_max <= (NT / ns) * REG;
+    // SEGD: NT / ns threads per segment, each holding up to KPT of its
+    // segment's entries (the order of a list is immaterial)
+    if constexpr (SEGD) seg_direct = ns <= NT && sh.list_n <= (NT / ns) * KPT;
     float* gv = a.gval + (long long)blockIdx.x * a.ld;
     int* gi = a.gidx + (long long)blockIdx.x * a.ld;
     for (int c0 = 0; c0 < (seg_direct ? 0 : tot); c0 += 8 * NT) {
@@ -246,6 +245,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   } else {
     len = row_length(a, r);
   }
+  constexpr int REG = KPT > 0 ? KPT : 1;
   uint32_t keys[REG];
   // rows longer than the register tile (possible for candidate lists) stream
   const bool regs = KPT > 0 && len <= REG * kSelectThreads;
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   if (KPT > 0 && regs) {
     // every load of the row at once (clamped addresses: no per-element branch)
     float v[REG];
-    if (seg_direct) {
+    if (SEGD && seg_direct) {
       const int ns = a.n_segs, tps = NT / ns;
       const int s = tid / tps, j0 = tid % tps;
       const int cs = s < ns ? sh.soff[s + 1] - sh.soff[s] : 0;
@@ -550,9 +550,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   for (int i = kk + tid; i < topk; i += kSelectThreads) out[i] = -1;
 }
 
-template <int NT, int KPT>
+template <int NT, int KPT, bool SEGD = false>
 static hipError_t launch_kpt(const SelectArgs& a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((select_kernel<NT, KPT, SEGD>), dim3(rows), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -609,6 +609,8 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
 }
 
 hipError_t launch_select_list(const SelectArgs& a, int n_launch_rows, int expect_len, hipStream_t st) {
+  if (a.seg_counts && expect_len > 256 * 32 && expect_len <= 1024 * 16)
+    return launch_kpt<1024, 16, true>(a, n_launch_rows, st);
   return launch_by_length(a, n_launch_rows, expect_len, st);
 }
 

@@ -55,11 +55,14 @@ DENSE = [
              seed=17, w_dist="int"),
     Workload("split_fp8_nq4_H16_d64_k2000", 1, 4, 2500, 16, 64, "fp8", "fp8", "normal8", "normal8",
              topk=2000, seed=18),
-    # every score of a query ties: every key of the prefix is a candidate, so
-    # the list segments overflow their threads' registers and the list select
-    # takes its gathering path (the other split cases load segments directly)
-    Workload("split_ties_const_keys_nq2_n20000_k300", 1, 2, 20000, 64, 128, "bf16", "bf16", "normal8", "const",
-             topk=300, seed=19),
+    # lists of 8193..16384 expected entries take the list select that loads
+    # segments directly: every segment fits (normal keys), and every score of
+    # a query ties so that every key is a candidate and the segments overflow
+    # into the gathering path (the shorter lists above always gather)
+    Workload("split_segd_nq2_n12000_k1500", 1, 2, 12000, 64, 128, "bf16", "bf16", "normal8", "heavy",
+             topk=1500, seed=19),
+    Workload("split_ties_const_keys_nq2_n20000_k1100", 1, 2, 20000, 64, 128, "bf16", "bf16", "normal8", "const",
+             topk=1100, seed=20),
 ]
 
 
