@@ -246,3 +246,41 @@ def test_refine_whole_prefix_equals_dense():
     dense = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **a)
     torch.cuda.synchronize()
     assert_same_sets(refine.cpu().numpy()[0], dense.cpu().numpy()[0], "refine(whole prefix) vs dense")
+
+
+def test_refine_candidates_split_over_column_chunks():
+    """A long caller-supplied candidate list (16700 slots, some empty) for one
+    group of 64 queries: with so few query blocks the Refine scan splits the
+    candidate columns over many workgroups, each staging its own slice of the
+    key indices in LDS.  Scores per slot within tolerance of the oracle, the
+    select bit-exact on the GPU's own scores, agreement with the oracle's
+    Refine on its own scores."""
+    dev = cuda()
+    wl = Workload("refine_C16700_H16_d64", 1, 64, 17000, 16, 64, "bf16", "bf16", "normal8", "heavy",
+                  topk=100, seed=23)
+    print(f"\n[refine] {wl.name}", flush=True)
+    inp = make_inputs(wl, dev)
+    G, C, K = 64, 16700, wl.topk
+    gen = torch.Generator(device="cpu").manual_seed(23)
+    cand = torch.randperm(wl.n_k, generator=gen)[:C].to(torch.int32)
+    cand[::97] = -1  # some empty slots
+    cand = cand.view(1, 1, C).to(dev)
+    ridx, rsc = S.refine_topk(inp["q"], inp["k"], inp["w"], cand, G, K, return_scores=True, **args(inp, wl))
+    torch.cuda.synchronize()
+    ridx, rsc, c = ridx.cpu().numpy()[0], rsc.cpu().numpy()[0], cand.cpu().numpy()[0, 0].astype(np.int64)
+    q, k, w = real_inputs(inp)
+    ref_sc = np.full((wl.n_q, C), -np.inf)
+    for t in range(wl.n_q):
+        ok = (c >= 0) & (c <= wl.q_pos0 + t)
+        ref_sc[t, ok] = np.maximum(k[0][c[ok]] @ q[0][t].T, 0.0) @ w[0][t]
+    check_scores(rsc, ref_sc, f"{wl.name} refine scores")
+    own = O.refine_topk(q[0], k[0], w[0], c[None], G, wl.q_pos0, K, scores=rsc.astype(np.float64))
+    assert_same_sets(ridx, own, f"{wl.name} refine select on own scores")
+    check_rows_valid(ridx, wl.q_pos0 + np.arange(wl.n_q), K)
+    ora = O.refine_topk(q[0], k[0], w[0], c[None], G, wl.q_pos0, K)
+    I = np.full((wl.n_q, wl.n_k), -np.inf)
+    for t in range(wl.n_q):
+        ok = (c >= 0) & (c <= wl.q_pos0 + t)
+        I[t, c[ok]] = ref_sc[t, ok]
+    agr = band_agreement(ridx, ora, I)
+    assert agr >= AGREEMENT, f"{wl.name}: refine agreement {agr}"
