@@ -103,12 +103,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, SelectShared& 
 // lists whose segments each fit their share of the threads' registers are
 // loaded from the segments directly (the decode lists' variant only: in the
 // others the extra path moves the register allocation of gathered rows into
-// spills).
+// spills).  FLIST: the variant for filtered candidate lists with their scan
+// records (the one-pass path, reading 16 entries per thread per batch); the
+// other variants do not contain that path.
 // A row's select is a chain of short dependent phases (loads, reductions,
 // histogram, scans), so rows in flight per CU decide its speed: 256-thread
 // workgroups are held to at least four waves per SIMD (at most 128 VGPRs,
 // four rows per CU; the LDS would allow five).
-template <int NT, int KPT, bool SEGD = false>
+template <int NT, int KPT, bool SEGD = false, bool FLIST = false>
 __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArgs a) {
   static_assert(!SEGD || KPT > 0, "direct segment loads fill registers");
   constexpr int kSelectThreads = NT;
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   }
   if (a.mode == kModeList) crow = a.lidx + (long long)blockIdx.x * a.ld;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  if (a.mode == kModeList && a.finfo) {
+  if (FLIST && a.mode == kModeList && a.finfo) {
     // A filtered list with its scan's record: one pass writes every
     // candidate above the boundary bin (there are exactly `above` of them),
     // collects the boundary bin's candidates (at most kFiltBoundaryMax), and
@@ -139,18 +141,18 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
       if (tid == 0) sh.list_n = 0;
       __syncthreads();
       int wbase = 0;
-      for (int c0 = 0; c0 < n; c0 += 8 * NT) {
-        uint32_t k[8];
-        int x[8], win = 0;
-        bool bnd[8], wn[8];
+      for (int c0 = 0; c0 < n; c0 += 16 * NT) {
+        uint32_t k[16];
+        int x[16], win = 0;
+        bool bnd[16], wn[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
           const int c = min(c0 + j * NT + tid, n - 1);
           k[j] = order_key(row[c]);
           x[j] = crow[c];
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
           const bool in = c0 + j * NT + tid < n;
           const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
           wn[j] = in && (all || bin > bstar);
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
         int tot;
         int pos = wbase + block_excl_scan<NT>(win, &tot, sh);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
           if (wn[j]) {
             if (pos < a.topk) out[pos] = x[j];
             ++pos;
@@ -550,9 +552,9 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   for (int i = kk + tid; i < topk; i += kSelectThreads) out[i] = -1;
 }
 
-template <int NT, int KPT, bool SEGD = false>
+template <int NT, int KPT, bool SEGD = false, bool FLIST = false>
 static hipError_t launch_kpt(const SelectArgs& a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NT, KPT, SEGD>), dim3(rows), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((select_kernel<NT, KPT, SEGD, FLIST>), dim3(rows), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -573,7 +575,8 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
   // candidate lists (up to a few k (1 + ln(n / k)) entries) are held 32 keys
   // per thread by 256-thread workgroups, more rows in flight per CU than
   // with 512 threads; a longer list streams inside the kernel
-  if (a.mode == kModeList) return launch_kpt<256, 32>(a, n_launch_rows, st);
+  if (a.mode == kModeList) return a.finfo ? launch_kpt<256, 32, false, true>(a, n_launch_rows, st)
+                                          : launch_kpt<256, 32>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
   const int classes[4] = {256 * 8, 256 * 32, 1024 * 16, 1024 * 32};
   long long r = 0;
