@@ -110,18 +110,25 @@ struct Layout {
   bool filter;  // dense scan with candidate filtering (see ScoreArgs::filter)
 };
 
+// The proxies' storage format (and so the proxy scan's q format).
+int proxy_q_dtype(const idx_problem* p) { return p->q_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
+
 Layout make_layout(int mode, const idx_problem* p, int n_rows, int n_cols, int group) {
   Layout L;
   L.mode = mode;
   L.n_rows = n_rows;
   L.n_cols = n_cols;
+  // float32 key tiles of d = 128 fit the LDS only up to 128 columns
+  // (two buffers of 256 would take 264 KiB): at least four row-waves then
+  const int scan_qf = mode == kModeProxy ? proxy_q_dtype(p) : p->q_dtype;
+  const int min_rw = (scan_qf == IDX_F32 && p->dim == 128) ? 4 : 2;
   if (mode == kModeGather) {
     const int seg = group < p->n_q ? group : p->n_q;
-    L.rw = pick_rw(seg, p->heads);
+    L.rw = std::max(pick_rw(seg, p->heads), min_rw);
     L.BQ = queries_per_block(L.rw, p->heads);
     L.total_blocks = p->batch * ceil_div(p->n_q, group) * ceil_div(group, L.BQ);
   } else {
-    L.rw = pick_rw(n_rows, p->heads);
+    L.rw = std::max(pick_rw(n_rows, p->heads), min_rw);
     L.nw = 8;
     L.filter = false;
     // Long dense scans with 64 heads (eight query-waves per workgroup, one
@@ -179,8 +186,13 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     }
     int kc = ceil_div(L.n_cols, chunks);
     kc = ceil_div(kc, tw) * tw;
-    // a gather workgroup stages its columns' key indices in LDS
-    if (L.mode == kModeGather && kc > kCandLdsMax) kc = kCandLdsMax;
+    // a gather workgroup stages its columns' key indices in LDS, beside the
+    // key tiles
+    if (L.mode == kModeGather) {
+      const size_t tiles = score_lds_bytes(qf, kf, D, L.rw, L.nw, 0, 0);
+      const int fit = (int)((kScoreLdsMax - tiles) / 4) / tw * tw;
+      kc = std::min(kc, std::min(kCandLdsMax, fit));
+    }
     chunks = ceil_div(L.n_cols, kc);
     sa.blk0 = blk0;
     sa.n_blocks = nb;
@@ -255,8 +267,6 @@ bool use_filter(const idx_problem* p, const Layout& L) { return L.filter && p->h
 size_t score_row_bytes(const idx_problem* p, const Layout& L) {
   return use_filter(p, L) ? (size_t)p->n_k * 8 + 16 : (size_t)p->n_k * 4;
 }
-
-int proxy_q_dtype(const idx_problem* p) { return p->q_dtype == IDX_F32 ? IDX_F32 : IDX_BF16; }
 
 size_t proxy_q_bytes(const idx_problem* p, int n_g) {
   return (size_t)p->batch * n_g * p->heads * p->dim * (proxy_q_dtype(p) == IDX_F32 ? 4 : 2);

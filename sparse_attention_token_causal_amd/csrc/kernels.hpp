@@ -101,6 +101,7 @@ struct SelectArgs {
 
 // Candidate columns one gather workgroup takes (their key indices are staged in LDS).
 constexpr int kCandLdsMax = 16384;
+constexpr size_t kScoreLdsMax = 160 * 1024;  // LDS of one score workgroup (the CU's whole LDS)
 size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int gather_cols);
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,
                         hipStream_t st);
@@ -125,9 +126,12 @@ constexpr int split_ops(int key_bytes, int d, int rwn) {
   return split_step_bytes(key_bytes, d) / 1024 / split_dma_waves(key_bytes, d, rwn) + (key_bytes == 1 ? 1 : 0);
 }
 constexpr int split_ring_steps(int key_bytes, int d, int rwn) {
-  // about 40 KiB of ring (two workgroups fit a CU), at least 4 steps
+  // about 40 KiB of ring (two workgroups fit a CU), at least 4 steps, or 3
+  // where 4 would take more than 64 KiB (bf16 keys of d = 128 with one
+  // row-wave: four column groups; the histograms of four rows need the rest)
   const int by_lds0 = (40 * 1024) / ((4 / rwn) * split_step_bytes(key_bytes, d));
-  const int by_lds = by_lds0 < 4 ? 4 : by_lds0;
+  const int min_steps = (4 / rwn) * split_step_bytes(key_bytes, d) * 4 <= 64 * 1024 ? 4 : 3;
+  const int by_lds = by_lds0 < min_steps ? min_steps : by_lds0;
   const int by_cnt = 2 + 63 / split_ops(key_bytes, d, rwn);                       // vmcnt holds 63
   const int p = by_lds < by_cnt ? by_lds : by_cnt;
   return p > 16 ? 16 : p;

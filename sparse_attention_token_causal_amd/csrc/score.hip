@@ -510,7 +510,7 @@ static hipError_t launch_mode(const ScoreArgs& a, dim3 grid, size_t lds, hipStre
   static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)score_kernel<QF, KF, H, D, RW, GATHER, NWV, FILTER>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kScoreLdsMax);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -570,6 +570,7 @@ hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_
   dim3 grid(a.n_blocks, n_col_chunks);
   if (a.mode == kModeGather && a.kc > kCandLdsMax) return hipErrorInvalidValue;
   const size_t lds = score_lds_bytes(qf, kf, D, a.rw, a.nw, a.filter, a.mode == kModeGather ? a.kc : 0);
+  if (lds > kScoreLdsMax) return hipErrorInvalidValue;
   if (qf == F32 && kf == F32) return pick_h<F32, F32>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == BF16) return pick_h<BF16, BF16>(a, H, D, grid, lds, st);
   if (qf == BF16 && kf == FP8) return pick_h<BF16, FP8>(a, H, D, grid, lds, st);

@@ -65,6 +65,37 @@ def check_scores(gpu, ref, what=""):
     return float(np.max(err / lim)) if e.any() else 0.0
 
 
+def ulp_bf16(x):
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 7)
+
+
+def run_absmax(x, bounds):
+    """Per run [a, b) of consecutive rows: the largest magnitude of each element."""
+    return np.stack([np.abs(x[a:b]).max(axis=0) for (a, b) in bounds])
+
+
+def check_stored_mean(gpu, ref, x, bounds, fmt, what):
+    """A mean over runs of rows of x, averaged in float32 and stored in `fmt`
+    (bf16 or f32), against the float64 mean rounded to that format.
+
+    Bound: one unit of the stored format at the larger of the two values,
+    plus the float32 accumulation error of a run of n members, each
+    conversion (scale product) and each of the n additions rounding once:
+    (n + 2) 2^-24 max|member|.  That second term governs when the members
+    cancel and the mean is near zero, where one unit of the stored format is
+    tiny."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    n = np.array([b - a for (a, b) in bounds], np.float64).reshape((-1,) + (1,) * (ref.ndim - 1))
+    acc = (n + 2) * 2.0 ** -24 * run_absmax(np.asarray(x, np.float64), bounds)
+    top = np.maximum(np.abs(gpu), np.abs(ref))
+    unit = ulp_bf16(top) if fmt == "bf16" else np.exp2(np.floor(np.log2(np.maximum(top, 1e-30))) - 23)
+    lim = unit * 1.0001 + acc
+    bad = np.abs(gpu - ref) > lim
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the stored-mean bound"
+
+
 def sets(rows):
     return [frozenset(int(x) for x in np.asarray(r).ravel() if x >= 0) for r in rows]
 

@@ -17,7 +17,7 @@ import oracle as O
 import sparse_attention_token_causal_amd as S
 from sparse_attention_token_causal_amd.synth import Workload, make_inputs
 
-from parity import assert_same_sets, check_rows_valid, check_scores, cuda, real_inputs, sets
+from parity import assert_same_sets, check_rows_valid, check_scores, check_stored_mean, cuda, real_inputs, sets
 
 pytestmark = pytest.mark.gpu
 
@@ -34,10 +34,6 @@ CASES = [
     (Workload("blk_bf16_L400_G32_block1", 1, 400, 400, 32, 64, "bf16", "bf16", "normal8", "heavy",
               topk=20, group=32, seed=35), 1, 50),
 ]
-
-
-def ulp_bf16(x):
-    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 7)
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
@@ -65,16 +61,12 @@ def test_block_route_parity(case):
         # block means and proxy: the rounded means
         mean = O.block_means(k[b], S_blk)
         qb, wb = O.proxy_means(q[b], w[b], G)
-        if wl.k_fmt == "f32":
-            assert np.allclose(km_f[b], mean, rtol=1e-6, atol=1e-7)
-        else:
-            ref, _ = O.round_proxy(mean, wb, "bf16")
-            assert (np.abs(km_f[b] - ref) <= ulp_bf16(ref) * 1.0001).all(), "block mean beyond 1 bf16 ulp"
-        if wl.q_fmt == "f32":
-            assert np.allclose(pq_f[b], qb, rtol=1e-6, atol=1e-7)
-        else:
-            ref, _ = O.round_proxy(qb, wb, "bf16")
-            assert (np.abs(pq_f[b] - ref) <= ulp_bf16(ref) * 1.0001).all(), "proxy beyond 1 bf16 ulp"
+        kfmt = "f32" if wl.k_fmt == "f32" else "bf16"
+        qfmt = "f32" if wl.q_fmt == "f32" else "bf16"
+        bb = [(j, min(j + S_blk, wl.n_k)) for j in range(0, wl.n_k, S_blk)]
+        check_stored_mean(km_f[b], O.round_proxy(mean, wb, kfmt)[0], k[b], bb, kfmt, f"block means b={b}")
+        check_stored_mean(pq_f[b], O.round_proxy(qb, wb, qfmt)[0], q[b], O.group_bounds(wl.n_q, G), qfmt,
+                          f"proxy b={b}")
         # block scores on the GPU's own proxy and block means
         c_ora, B_ora, _ = O.block_route(pq_f[b], pw_f[b], km_f[b], lim, wl.n_k, S_blk, n_sel)
         check_scores(bsc[b], B_ora, f"{wl.name} block scores b={b}")

@@ -33,8 +33,8 @@ import oracle as O
 import sparse_attention_token_causal_amd as S
 from sparse_attention_token_causal_amd.synth import Workload, make_inputs
 
-from parity import AGREEMENT, assert_same_sets, band_agreement, check_rows_valid, check_scores, cuda, \
-    real_inputs, sets
+from parity import AGREEMENT, assert_same_sets, band_agreement, check_rows_valid, check_scores, \
+    check_stored_mean, cuda, real_inputs, sets
 
 pytestmark = pytest.mark.gpu
 
@@ -182,11 +182,9 @@ def test_ivf_route_parity(case):
     lim = O.proxy_limits(wl.n_q, G, wl.q_pos0)
     for b in range(wl.batch):
         qb, wb = O.proxy_means(q[b], w[b], G)
-        if wl.q_fmt == "f32":
-            assert np.allclose(pq_f[b], qb, rtol=1e-6, atol=1e-7)
-        else:
-            ref, _ = O.round_proxy(qb, wb, "bf16")
-            assert (np.abs(pq_f[b] - ref) <= ulp_bf16(ref) * 1.0001).all(), "proxy beyond 1 bf16 ulp"
+        qfmt = "f32" if wl.q_fmt == "f32" else "bf16"
+        check_stored_mean(pq_f[b], O.round_proxy(qb, wb, qfmt)[0], q[b], O.group_bounds(wl.n_q, G), qfmt,
+                          f"proxy b={b}")
         # cluster scores on the GPU's own proxy and centroids
         S_ref = np.full((lim.size, m), -np.inf)
         for g in range(lim.size):
