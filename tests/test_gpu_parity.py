@@ -15,7 +15,7 @@ import sparse_attention_token_causal_amd as S
 from sparse_attention_token_causal_amd.synth import Workload, WORKLOADS, make_inputs
 
 from parity import (AGREEMENT, assert_same_sets, band_agreement, check_rows_valid, check_scores, check_stored_mean,
-                    cuda, real_inputs)
+                    cuda, real_inputs, score_magnitudes)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,14 +86,15 @@ def test_dense_parity(wl):
     worst = 0.0
     for b in range(wl.batch):
         I = O.dense_scores(q[b], k[b], w[b], wl.q_pos0)
-        worst = max(worst, check_scores(sc[b], I, f"{wl.name} b={b}"))
+        M = score_magnitudes(q[b], k[b], w[b]) if (w[b] < 0).any() else None
+        worst = max(worst, check_scores(sc[b], I, f"{wl.name} b={b}", mag=M))
         # select on the GPU's own scores: bit-exact
         own = _select_rows(sc[b], wl.q_pos0, wl.topk)
         assert_same_sets(idx[b], own, f"{wl.name} b={b} select on own scores")
         lim = wl.q_pos0 + np.arange(wl.n_q)
         check_rows_valid(idx[b], lim, wl.topk, np.minimum(wl.topk, lim + 1))
         ora = O.dense_topk(q[b], k[b], w[b], wl.q_pos0, wl.topk, scores=I)
-        agr = band_agreement(idx[b], ora, I)
+        agr = band_agreement(idx[b], ora, I, mag_rows=None if M is None else M.max(axis=1))
         assert agr >= AGREEMENT, f"{wl.name}: set agreement {agr}"
     print(f"  worst err/tol {worst:.3g}", flush=True)
 
@@ -188,26 +189,32 @@ def test_grouped_parity(wl):
         check_stored_mean(pw_f[b], wr, w[b], gb, "f32", f"{wl.name} proxy w b={b}")
         # G2: proxy scores on the GPU's own proxy
         P = O.proxy_scores(pq_f[b], pw_f[b], k[b], lim)
-        check_scores(ps[b], P, f"{wl.name} proxy scores b={b}")
+        signed = (w[b] < 0).any()
+        check_scores(ps[b], P, f"{wl.name} proxy scores b={b}",
+                     mag=score_magnitudes(pq_f[b], k[b], pw_f[b]) if signed else None)
         # G3: candidates = oracle select on the GPU's proxy scores
         own = O.proxy_candidates(ps[b].astype(np.float64), lim, C)
         assert_same_sets(cand[b], own, f"{wl.name} candidates b={b}")
         check_rows_valid(cand[b], lim, C, np.minimum(C, lim + 1))
         # G4: refine scores per candidate slot
         I = O.dense_scores(q[b], k[b], w[b], wl.q_pos0)
+        M = score_magnitudes(q[b], k[b], w[b]) if signed else None
         ref_sc = np.full((wl.n_q, C), -np.inf)
+        ref_mag = np.zeros((wl.n_q, C))
         for t in range(wl.n_q):
             c = cand[b, t // G]
             ok = (c >= 0) & (c <= wl.q_pos0 + t)
             ref_sc[t, ok] = I[t, c[ok]]
-        check_scores(rsc[b], ref_sc, f"{wl.name} refine scores b={b}")
+            if signed:
+                ref_mag[t, ok] = M[t, c[ok]]
+        check_scores(rsc[b], ref_sc, f"{wl.name} refine scores b={b}", mag=ref_mag if signed else None)
         # G5: refine select on the GPU's own scores
         own = O.refine_topk(q[b], k[b], w[b], cand[b], G, wl.q_pos0, K, scores=rsc[b].astype(np.float64))
         assert_same_sets(ridx[b], own, f"{wl.name} refine select b={b}")
         check_rows_valid(ridx[b], wl.q_pos0 + np.arange(wl.n_q), K)
         # G6: agreement with the oracle's refine on oracle scores
         ora = O.refine_topk(q[b], k[b], w[b], cand[b], G, wl.q_pos0, K)
-        agr = band_agreement(ridx[b], ora, I)
+        agr = band_agreement(ridx[b], ora, I, mag_rows=M.max(axis=1) if signed else None)
         assert agr >= AGREEMENT, f"{wl.name}: refine agreement {agr}"
         # G7: reuse is integer work: exact, in the proxy's order
         ora_u = O.reuse_topk(ptop[b], G, wl.q_pos0, wl.n_q, K)
