@@ -225,8 +225,9 @@ int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int3
  *   out_assign    optional [B, n_v, n_k] int32: the list of every key of the
  *                 window, -1 beyond it.
  * IDX_EINVAL for n_clusters outside [1, 1024], refit < n_clusters or not a
- * multiple of 128, iters outside [0, 64], a null required output.  With
- * n_k < R nothing is enqueued.  ws: idx_workspace_bytes(p, IDX_OP_IVF_BUILD,
+ * multiple of 128, iters outside [0, 64], or a null required output when
+ * n_v >= 1.  With n_k < R (n_v = 0) the outputs are empty, any pointer may
+ * be null and nothing is enqueued.  ws: idx_workspace_bytes(p, IDX_OP_IVF_BUILD,
  * 0, n_clusters, 0).
  *
  * idx_ivf_route: group g (as in idx_group_proxy_scan, last member at

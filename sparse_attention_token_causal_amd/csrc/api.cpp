@@ -786,9 +786,9 @@ int32_t idx_ivf_build(const idx_problem* p, int32_t n_clusters, int32_t refit, i
   if (rc != IDX_OK) return rc;
   const int m = n_clusters, R = refit;
   if (!ivf_params_ok(m, R) || iters < 0 || iters > 64) return IDX_EINVAL;
-  if (!out_centroids || !out_offsets || !out_members || !out_counts) return IDX_EINVAL;
   const int n_v = p->n_k / R;
-  if (n_v == 0) return IDX_OK;  // no refit point inside the keys: nothing to publish
+  if (n_v == 0) return IDX_OK;  // no refit point inside the keys: the outputs are empty
+  if (!out_centroids || !out_offsets || !out_members || !out_counts) return IDX_EINVAL;
   const IvfBuildLayout L = ivf_build_layout(p, m);
   if (!ws || ws_bytes < L.total) return IDX_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;

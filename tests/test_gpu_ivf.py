@@ -52,6 +52,12 @@ CASES = [
               topk=100, group=2, seed=44), 64, 1024, 2, 256, 2048),
     (Workload("ivf_bf16_L1300_H32_d64_m1024", 1, 1300, 1300, 32, 64, "bf16", "bf16", "normal8", "heavy",
               topk=20, group=32, seed=45), 1024, 1024, 1, 128, 1024),
+    # one cluster: every key in the single list
+    (Workload("ivf_m1_decode_bf16_B2_n4370", 2, 3, 4370, 64, 128, "bf16", "bf16", "ar1", "heavy", rho=0.98,
+              topk=132, group=36, seed=47), 1, 2048, 1, 256, 3686),
+    # keys shorter than the refit interval: no version, empty index arrays
+    (Workload("ivf_short_bf16_L600_R1024_noversion", 1, 600, 600, 32, 64, "bf16", "bf16", "normal8", "heavy",
+              topk=20, group=8, seed=46), 64, 1024, 1, 128, 1024),
 ]
 
 
@@ -112,7 +118,7 @@ def check_index(idx, k, R, what):
             chosen = d2[np.arange(win), a[:win]]
             assert (chosen - best <= tol).all(), f"{what}: a key assigned beyond the rounding of its distance"
             srt = np.sort(d2, axis=1)
-            clear = (srt[:, 1] - srt[:, 0]) > 2 * tol
+            clear = (srt[:, 1] - srt[:, 0]) > 2 * tol if m > 1 else np.ones(win, bool)
             assert (a[:win][clear] == d2.argmin(axis=1)[clear]).all(), f"{what}: a clear nearest centroid missed"
             row.append((C, a))
         out.append(row)
@@ -143,7 +149,7 @@ def test_ivf_build_parity(case):
     torch.cuda.synchronize()
     n_v = wl.n_k // R
     views = {t: check_index(idx, k, R, f"{wl.name} T={t}") for t, idx in builds.items()}
-    for b in range(wl.batch):
+    for b in range(wl.batch if n_v >= 1 else 0):
         init = stored(k[b][(np.arange(m) * R) // m], wl.k_fmt)
         for v in range(n_v):  # no iteration: every version keeps the initial keys
             close_stored(views[0][b][v][0], init, wl.k_fmt, scale, f"{wl.name} T=0 v={v}")
