@@ -135,7 +135,8 @@ def make_step(S, wl, inp, dev):
 
 def cpu_baseline(wl, inp, seconds):
     """The oracle as it stands, on evenly spaced queries of the same inputs,
-    until about `seconds` of CPU work; returns the JSON object."""
+    sequence after sequence, until about `seconds` of CPU work or the whole
+    workload (the decode workloads are small); returns the JSON object."""
     import numpy as np
     import oracle as O
     from sparse_attention_token_causal_amd import synth
@@ -145,9 +146,6 @@ def cpu_baseline(wl, inp, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:  # threadpoolctl missing: report the affinity set
         threads = len(os.sched_getaffinity(0))
-    b = 0
-    ks = None if inp["k_scale"] is None else inp["k_scale"][b].cpu().numpy()
-    k = O.real_values(synth.raw_numpy(inp["k"][b]), synth.fmt_of(inp["k"]), ks)
     n = wl.n_q
     order = []
     # evenly spaced queries, refined by bisection so any prefix of the list is spread out
@@ -163,28 +161,39 @@ def cpu_baseline(wl, inp, seconds):
         step //= 2
     pairs = 0
     done = 0
-    t0 = time.perf_counter()
-    for t in order:
-        qs = None if inp["q_scale"] is None else inp["q_scale"][b, t:t + 1].cpu().numpy()
-        q = O.real_values(synth.raw_numpy(inp["q"][b, t:t + 1]), synth.fmt_of(inp["q"]), qs)
-        w = inp["w"][b, t:t + 1].cpu().numpy().astype(np.float64)
-        lim = np.array([wl.q_pos0 + t])
-        I = O.causal_scores(q, k, w, lim)
-        O.select_topk(I[0, : lim[0] + 1], np.arange(lim[0] + 1), wl.topk)
-        pairs += int(lim[0]) + 1
-        done += 1
-        if time.perf_counter() - t0 > seconds:
+    el = 0.0
+    seqs = 0
+    for b in range(wl.batch):
+        ks = None if inp["k_scale"] is None else inp["k_scale"][b].cpu().numpy()
+        k = O.real_values(synth.raw_numpy(inp["k"][b]), synth.fmt_of(inp["k"]), ks)
+        seqs += 1
+        t0 = time.perf_counter()
+        for t in order:
+            qs = None if inp["q_scale"] is None else inp["q_scale"][b, t:t + 1].cpu().numpy()
+            q = O.real_values(synth.raw_numpy(inp["q"][b, t:t + 1]), synth.fmt_of(inp["q"]), qs)
+            w = inp["w"][b, t:t + 1].cpu().numpy().astype(np.float64)
+            lim = np.array([wl.q_pos0 + t])
+            I = O.causal_scores(q, k, w, lim)
+            O.select_topk(I[0, : lim[0] + 1], np.arange(lim[0] + 1), wl.topk)
+            pairs += int(lim[0]) + 1
+            done += 1
+            if el + time.perf_counter() - t0 > seconds:
+                break
+        el += time.perf_counter() - t0
+        if el > seconds:
             break
-    el = time.perf_counter() - t0
+    whole = seqs == wl.batch and done == wl.batch * n
+    what = "every query of every sequence" if whole else f"{done} evenly spaced queries of {seqs} sequence(s)"
     return {"value": pairs / el, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} evenly spaced queries of sequence 0 ({pairs} causal pairs, "
-                      f"float64 NumPy, {el:.1f} s); queries/s {done / el:.3g}"}
+            "sample": f"{what} ({pairs} causal pairs, float64 NumPy, {el:.1f} s, key decoding "
+                      f"excluded); queries/s {done / el:.3g}"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for a decode workload, 20 otherwise)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -220,6 +229,9 @@ def main():
     inp = make_inputs(wl, dev)
     torch.cuda.synchronize()
     step, pairs, flops, queries, dtype, kind = make_step(S, wl, inp, dev)
+    # enough steps that the first launch's latency is spread thin: a decode
+    # step is about 75 us of device time
+    steps = args.steps if args.steps is not None else (200 if kind == "decode" else 20)
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -229,19 +241,19 @@ def main():
     # launch (on the launch stream); the events add a few microseconds per
     # launch, which matters for the short decode step, so they stay out of
     # the step time.
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] timing {steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    s_per_step = (t1 - t0) / args.steps
+    s_per_step = (t1 - t0) / steps
     S.profile_read()  # drop anything recorded before
     S.profile_enable(True)
     torch.cuda.synchronize()
-    log(f"[bench] timing the kernels of {args.steps} more steps (HIP events per launch)")
+    log(f"[bench] timing the kernels of {steps} more steps (HIP events per launch)")
     t2 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
@@ -250,7 +262,7 @@ def main():
     score_ms, score_n = prof["score"]
     sel_ms, sel_n = prof["select"]
     per_launch_ms = score_ms / max(score_n, 1)
-    launches_per_step = score_n / args.steps
+    launches_per_step = score_n / steps
     flops_per_launch = flops / max(launches_per_step, 1e-9)
     achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
@@ -277,7 +289,7 @@ def main():
         "value": pairs / s_per_step,
         "unit": "pairs/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": s_per_step * 1e3,
         "higher_is_better": True,
@@ -290,8 +302,8 @@ def main():
                    "k_storage": wl.k_fmt, "parallelism": "single GPU"},
         "queries_per_s": queries / s_per_step,
         "pairs_per_step": pairs,
-        "kernels_ms_per_step": {k: v[0] / args.steps for k, v in prof.items() if v[1]},
-        "ms_per_step_with_kernel_events": (t3 - t2) / args.steps * 1e3,
+        "kernels_ms_per_step": {k: v[0] / steps for k, v in prof.items() if v[1]},
+        "ms_per_step_with_kernel_events": (t3 - t2) / steps * 1e3,
         "roofline": roof,
         "cpu_baseline": None,
     }
