@@ -48,6 +48,10 @@
  *    aliasing between outputs and inputs, n_k < 2^31.  Calls on distinct
  *    workspaces are independent; two calls that share a workspace must be
  *    ordered on one stream.
+ *  - HIP graph capture: a call may be captured on `stream` once the same
+ *    call shape (dtypes, heads, dim, mode) has run once uncaptured on the
+ *    device, since the first launch of some kernels sets their LDS limit
+ *    (hipFuncSetAttribute).  Capture with profiling off (idx_profile_enable).
  */
 #ifndef SATC_IDX_H
 #define SATC_IDX_H
