@@ -19,7 +19,7 @@ import oracle as O
 import sparse_attention_token_causal_amd as S
 from sparse_attention_token_causal_amd.synth import WORKLOADS, make_inputs
 
-from parity import (AGREEMENT, assert_same_sets, band_agreement, check_rows_valid, check_scores,
+from parity import (AGREEMENT, ATOL, RTOL, assert_same_sets, band_agreement, check_rows_valid, check_scores,
                     cuda, real_rows)
 
 pytestmark = pytest.mark.gpu
@@ -212,14 +212,23 @@ def grouped_fullsize(wl, sample_groups, dense_queries):
     dense = np.array(dense)
     rec_ref = O.recall(ridx_np[0, dense_queries], dense)
     rec_reu = O.recall(uidx_np[0, dense_queries], dense)
-    # Refine recovers the dense members that are candidates (up to float32
-    # near-ties at the k-th score): report the largest deviation from that identity
+    # Refine keeps every dense member that is a candidate (the candidate-coverage
+    # identity), except where float32 and float64 order near-ties at the k-th
+    # score differently: a member it misses lies within twice the score
+    # tolerance of the k-th dense score (with every score within tolerance, K
+    # candidates outscoring it on the GPU would otherwise all be dense members
+    # besides it, one too many)
     dev_id = 0.0
     for i, t in enumerate(dense_queries):
-        D = set(int(x) for x in dense[i] if x >= 0)
+        d_i = [int(x) for x in dense[i] if x >= 0]
+        D = set(d_i)
         V = set(int(x) for x in cand_np[t // G] if 0 <= x <= wl.q_pos0 + t)
+        Rf = set(int(x) for x in ridx_np[0, t] if x >= 0)
+        tau = I[i, d_i[-1]]
+        for s in (D & V) - Rf:
+            assert abs(I[i, s] - tau) <= 2 * (ATOL + RTOL * abs(tau)), \
+                f"query {t}: dense member {s} (score {I[i, s]}, k-th {tau}) is a candidate Refine missed"
         dev_id = max(dev_id, abs(rec_ref[i] - len(D & V) / len(D)))
-    assert dev_id < 0.01, f"Refine recall departs from the candidate-coverage identity by {dev_id}"
     print(f"  Refine recall vs dense: mean {rec_ref.mean():.4f} min {rec_ref.min():.4f}; "
           f"Reuse recall: mean {rec_reu.mean():.4f}; identity deviation {dev_id:.2e}", flush=True)
 
