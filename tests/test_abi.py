@@ -132,6 +132,8 @@ def test_ivf_invalid_arguments(lib):
     short = problem(n_q=100, n_k=100)
     assert ivf_route_call(lib, short, index=(None,) * 4, ws=None, ws_bytes=0) == -3
     assert ivf_build_call(lib, short, ws=None, ws_bytes=0) == 0  # nothing to build, nothing enqueued
+    # ... and its outputs are empty, so they may be null (as empty tensors' pointers are)
+    assert ivf_build_call(lib, short, outs=(None,) * 4, ws=None, ws_bytes=0) == 0
 
 
 def test_ivf_workspace_sizes(lib):
