@@ -106,7 +106,13 @@ hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* 
 
 // One wave per query: filter the group's shared list to the query's causal
 // prefix and compact it in order (ballot + popcount prefix), then pad.
-// HBM-write-bound: every member writes a full row of topk indices.
+// HBM-write-bound: every member writes a full row of topk indices.  The list
+// is read in tiles of kReuseChunks x 64 entries whose loads are all issued
+// before the first ballot, so a row costs about one load latency per tile
+// rather than one per 64 entries (the lists are shared by the group's
+// members and come from the L2).
+constexpr int kReuseChunks = 16;
+
 __global__ __launch_bounds__(256) void reuse_kernel(const int* ptop, int n_q, int q_pos0, int group,
                                                     int topk, int* out) {
   const int wave = threadIdx.x / kWave, lane = lane_id();
@@ -118,13 +124,20 @@ __global__ __launch_bounds__(256) void reuse_kernel(const int* ptop, int n_q, in
   const int pos = q_pos0 + t;
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   int base = 0;
-  for (int c0 = 0; c0 < topk; c0 += kWave) {
-    const int c = c0 + lane;
-    const int v = c < topk ? src[c] : -1;
-    const bool keep = v >= 0 && v <= pos;
-    const unsigned long long m = __ballot(keep);
-    if (keep) dst[base + __popcll(m & lt)] = v;
-    base += __popcll(m);
+  for (int c0 = 0; c0 < topk; c0 += kReuseChunks * kWave) {
+    int v[kReuseChunks];
+#pragma unroll
+    for (int j = 0; j < kReuseChunks; ++j) {
+      const int c = c0 + j * kWave + lane;
+      v[j] = c < topk ? src[c] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kReuseChunks; ++j) {
+      const bool keep = v[j] >= 0 && v[j] <= pos;
+      const unsigned long long m = __ballot(keep);
+      if (keep) dst[base + __popcll(m & lt)] = v[j];
+      base += __popcll(m);
+    }
   }
   for (int i = base + lane; i < topk; i += kWave) dst[i] = -1;
 }
