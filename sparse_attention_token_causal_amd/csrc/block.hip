@@ -65,33 +65,46 @@ hipError_t launch_block_means(const void* k, const float* k_scale, int B, int n_
 // (n_sel + 1) * block): the u-th key of the (i / block)-th routed block while
 // routed blocks last, then the keys of the trailing partial block of the
 // group's prefix, then -1.  The routed blocks come first in `sel` (the select
-// pads its rows at the end).
+// pads its rows at the end), so their number is the count of valid entries.
+// Each thread issues the loads of eight slots before storing them.
+constexpr int kExpandBatch = 8;
+
 __global__ __launch_bounds__(256) void block_expand_kernel(const int* sel, int n_q, int q_pos0, int group,
                                                            int block, int n_sel, int* cand) {
-  __shared__ int s_n;
-  const int g = blockIdx.x, b = blockIdx.y;
+  __shared__ int s_cnt[4];
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int n_g = (n_q + group - 1) / group;
   const int* srow = sel + ((size_t)b * n_g + g) * n_sel;
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < n_sel && srow[n] >= 0) ++n;
-    s_n = n;
-  }
+  int cnt = 0;
+  for (int i = tid; i < n_sel; i += 256) cnt += srow[i] >= 0 ? 1 : 0;
+  cnt = wave_sum(cnt);
+  if (lane_id() == 0) s_cnt[tid / kWave] = cnt;
   __syncthreads();
-  const int n_routed = s_n;
+  const int n_routed = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
   const int last = mode_limit(kModeProxy, q_pos0, n_q, group, block, g);  // pos(t_last)
   const int n_full = (last + 1) / block;
   const int tail = last + 1 - n_full * block;
   const int width = (n_sel + 1) * block;
   int* crow = cand + ((size_t)b * n_g + g) * width;
-  for (int i = threadIdx.x; i < width; i += blockDim.x) {
-    const int j = i / block, u = i % block;
-    int key = -1;
-    if (j < n_routed)
-      key = srow[j] * block + u;
-    else if (i - n_routed * block < tail)
-      key = n_full * block + (i - n_routed * block);
-    crow[i] = key;
+  for (int i0 = 0; i0 < width; i0 += kExpandBatch * 256) {
+    int key[kExpandBatch];
+#pragma unroll
+    for (int j = 0; j < kExpandBatch; ++j) {
+      const int i = i0 + j * 256 + tid;
+      const int blk = i / block, u = i % block;
+      key[j] = -1;
+      if (i < width) {
+        if (blk < n_routed)
+          key[j] = srow[blk] * block + u;
+        else if (i - n_routed * block < tail)
+          key[j] = n_full * block + (i - n_routed * block);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kExpandBatch; ++j) {
+      const int i = i0 + j * 256 + tid;
+      if (i < width) crow[i] = key[j];
+    }
   }
 }
 

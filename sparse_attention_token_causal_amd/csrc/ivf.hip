@@ -467,23 +467,38 @@ __global__ __launch_bounds__(256) void ivf_expand_kernel(IvfRouteArgs a) {
   const int P = sPre[n_take];
   const int* off = a.offsets + ver * (m + 1);
   const int* mem = a.members + ver * a.n_k;
-  for (int i = tid; i < a.n_cand; i += blockDim.x) {
-    int key = -1;
-    if (i < P) {
-      int lo = 0, hi = n_take - 1;  // last rank r with sPre[r] <= i
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sPre[mid] <= i)
-          lo = mid;
-        else
-          hi = mid - 1;
+  // the taken clusters' list offsets, in walk order (in the sizes' storage:
+  // the prefix sums above were their last use, and barriers separate them)
+  int* sOff = sSz;
+  for (int r = tid; r < n_take; r += 256) sOff[r] = off[sOrd[r]];
+  __syncthreads();
+  // each thread issues the member loads of eight slots before storing them
+  constexpr int XB = 8;
+  for (int i0 = 0; i0 < a.n_cand; i0 += XB * 256) {
+    int key[XB];
+#pragma unroll
+    for (int j = 0; j < XB; ++j) {
+      const int i = i0 + j * 256 + tid;
+      key[j] = -1;
+      if (i < P) {
+        int lo = 0, hi = n_take - 1;  // last rank r with sPre[r] <= i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sPre[mid] <= i)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        key[j] = mem[sOff[lo] + (i - sPre[lo])];
+      } else if (i < P + tail) {
+        key[j] = e + (i - P);
       }
-      const int c = sOrd[lo];
-      key = mem[off[c] + (i - sPre[lo])];
-    } else if (i < P + tail) {
-      key = e + (i - P);
     }
-    crow[i] = key;
+#pragma unroll
+    for (int j = 0; j < XB; ++j) {
+      const int i = i0 + j * 256 + tid;
+      if (i < a.n_cand) crow[i] = key[j];
+    }
   }
 }
 
