@@ -11,6 +11,14 @@ for the invariants; sampled rows of the first and last sequence against the
 oracle: scores within tolerance, the select bit-exact on the GPU's own
 scores, banded set agreement with the oracle's own top-k, and the timed
 (no score dump) path equal to the dump path.
+
+Grouped shapes (PIVOT: proxy scan, Refine, Reuse) are drawn the same way,
+with group sizes 1-256 or the decode grouping (the few queries at the end
+of the keys as one group), candidate budgets from k + G - 1 to 4k + G, and
+clustered keys besides; they run the full-size grouped checks (every row's
+invariants, Reuse exact, sampled groups' proxy scores, candidates, Refine
+scores and select against the oracle, the Refine candidate-coverage
+identity up to near-ties).
 """
 
 import gc
@@ -25,7 +33,7 @@ from sparse_attention_token_causal_amd.synth import Workload, make_inputs
 
 from parity import (AGREEMENT, assert_same_sets, band_agreement, check_scores, cuda, real_rows,
                     score_magnitudes)
-from test_gpu_fullsize import all_rows_valid, sample_rows
+from test_gpu_fullsize import all_rows_valid, grouped_fullsize, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -93,5 +101,45 @@ def test_large_random_shape(wl):
         agr = band_agreement(idd, ora, I, mag_rows=M.max(axis=1) if signed else None)
         assert agr >= AGREEMENT, f"{wl.name} b={b}: set agreement {agr}"
     del sc, idx_d, inp
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _draw_grouped(rng, i):
+    qf, kf = COMBOS[int(rng.integers(len(COMBOS)))]
+    H = int(rng.choice([16, 32, 64]))
+    d = int(rng.choice([64, 128]))
+    if rng.random() < 0.3:  # decode grouping
+        n_q = int(rng.integers(1, 5))
+        n_k, G = int(rng.integers(40000, 300001)), n_q
+    else:
+        n_q = int(rng.integers(3000, 70001))
+        n_k = n_q if rng.random() < 0.7 else int(rng.integers(n_q, n_q + 20000))
+        G = int(rng.choice([1, 2, 7, 16, 33, 64, 128, 256]))
+    pairs = (1e12 if qf == "f32" else 2e13) / (2 * H * d)  # proxy-scan pairs per call
+    if n_q >= 5 and n_q * (n_k - n_q / 2) / G > pairs:
+        n_q = n_k = int((2 * pairs * G) ** 0.5)
+    kd = str(rng.choice(["normal8", "heavy", "int", "clustered"]))
+    qd = "int" if kd == "int" else str(rng.choice(["normal8", "ar1"]))
+    K = int(rng.integers(1, 64) if rng.random() < 0.2 else rng.integers(64, 4097))
+    C = int(rng.integers(K + G - 1, 4 * K + G + 1))
+    kw = dict(rho=0.98 if qd == "ar1" else 0.0, topk=K, seed=24000 + i, w_dist="int" if kd == "int" else "uniform",
+              group=G, n_cand=C)
+    if kd == "clustered":
+        kw.update(clusters=int(rng.integers(2, 512)), seed_stride=0)
+    name = f"rlg{i}_q{n_q}_k{n_k}_H{H}_d{d}_{qf}{kf}_{qd}-{kd}_k{K}_G{G}_C{C}"
+    return Workload(name, 1, n_q, n_k, H, d, qf, kf, qd, kd, **kw)
+
+
+_RNG_G = np.random.default_rng(20261206)  # a draw that covers every class listed above
+LARGE_GROUPED = [_draw_grouped(_RNG_G, i) for i in range(6)]
+
+
+@pytest.mark.parametrize("wl", LARGE_GROUPED, ids=[w.name for w in LARGE_GROUPED])
+def test_large_random_grouped_shape(wl):
+    n_g = -(-wl.n_q // wl.group)
+    groups = sorted({0, n_g // 3, n_g - 1})
+    queries = sorted({int(x) for x in np.linspace(wl.n_q // 4, wl.n_q - 1, 5)})
+    grouped_fullsize(wl, groups, queries)
     gc.collect()
     torch.cuda.empty_cache()
