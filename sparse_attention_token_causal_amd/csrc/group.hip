@@ -84,8 +84,16 @@ __global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const f
     }
   }
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
-    float s = 0.f;
-    for (int t = t0; t < t1; ++t) s += w[((size_t)b * n_q + t) * H + h];
+    float s = 0.f;  // member order, eight loads in flight
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = w[((size_t)b * n_q + t + u) * H + h];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
+    }
+    for (; t < t1; ++t) s += w[((size_t)b * n_q + t) * H + h];
     pw[prow * H + h] = s / n;
   }
 }
