@@ -201,10 +201,11 @@ int32_t idx_block_route(const idx_problem* p, int32_t group, int32_t block, int3
  * idx_refine_topk ("AttentionIndex Architecture ...", "KEY FINDINGS" and "An
  * Inverted File With Causal Versions": keys are grouped by similarity into
  * inverted lists, a query is routed to the lists whose representatives score
- * highest and the native indexer re-scores their members; new keys are added
- * to the lists in small batches; periodic refits regroup the whole prefix
- * starting from the previous clustering and publish a new version; a query
- * uses a version only if every key that built it lies in its prefix).  The
+ * highest and the native indexer re-scores their members; arriving keys
+ * join existing lists batch by batch, and a refit now and then reclusters all
+ * keys so far, seeded with the previous clustering, as a new version; a group
+ * routes through a version only when all of that version's keys precede its
+ * last member).  The
  * representatives here are plain means (no trained encoder).
  *
  * idx_ivf_build: for each sequence, versions u = 1 .. n_v = floor(n_k / R)

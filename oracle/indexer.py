@@ -288,11 +288,11 @@ def block_reference(q, k, w, q_pos0, group, block, n_sel, topk, q_fmt, k_fmt):
 # Causal Versions" and "Worked Example: Blocks Lose, Clusters Win": keys are
 # grouped by similarity into inverted lists, a query is routed to the lists
 # whose representatives score highest and the native indexer re-scores their
-# members.  New keys become searchable at once and are added to the lists in
-# small batches; periodic refits regroup the whole prefix starting from the
-# previous clustering and publish a new version (lists and representatives
-# together); a query uses a version only if every key that built it lies in
-# its prefix.  Readings (the pages leave them open; no trained encoder here,
+# members.  Arriving keys are candidates right away and join existing lists
+# batch by batch; now and then a refit reclusters all keys so far, seeded with
+# the previous clustering, giving a new version of lists and representatives;
+# causality holds per version: a group may use a version only when all of the
+# keys behind it precede the group's last member.  Readings (the pages leave them open; no trained encoder here,
 # so representatives are plain means):
 #   * refits happen every R keys: version u (u = 1, 2, ...) is refit on keys
 #     [0, u R) by T Lloyd iterations of k-means with m centroids, starting

@@ -1,7 +1,8 @@
 """Causal lightning indexer and PIVOT group-shared indexing on MI355X (gfx950).
 
 Thin ctypes binding over the C ABI declared in ``include/idx.h``: it checks
-tensor shapes and devices, allocates outputs and workspace with torch, and
+tensor shapes, dtypes, contiguity and devices (caller-supplied ``out`` and
+``workspace`` tensors included), allocates outputs and workspace with torch, and
 passes raw device pointers and the current HIP stream.  Every step of the
 computation runs in the library's HIP kernels; there is no other path, and
 the functions raise if the library has not been built.
@@ -142,6 +143,30 @@ def workspace_bytes(p, op, group=0, n_cand=0, topk=0):
     return int(load_library().idx_workspace_bytes(ctypes.byref(p), op, group, n_cand, topk))
 
 
+def _check_out(out, shape, like, name="out"):
+    """A caller-supplied int32 output: exactly `shape`, contiguous, on `like`'s
+    device (the kernels write every element of it).  None -> a new tensor."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.int32, device=like.device)
+    if not isinstance(out, torch.Tensor) or out.dtype != torch.int32 or tuple(out.shape) != tuple(shape) \
+            or not out.is_contiguous():
+        raise IndexerError(f"{name} must be a contiguous int32 tensor of shape {list(shape)}")
+    if out.device != like.device:
+        raise IndexerError(f"{name} must be on {like.device}, not {out.device}")
+    return out
+
+
+def _check_workspace_tensor(workspace, like):
+    """A caller-supplied workspace: a contiguous 1-D uint8 tensor on `like`'s device."""
+    if workspace is None:
+        return
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or workspace.dim() != 1 \
+            or not workspace.is_contiguous():
+        raise IndexerError("workspace must be a contiguous 1-D uint8 tensor (its length is its size in bytes)")
+    if workspace.device != like.device:
+        raise IndexerError(f"workspace must be on {like.device}, not {workspace.device}")
+
+
 def _workspace(p, op, device, group=0, n_cand=0, topk=0, workspace=None):
     n = workspace_bytes(p, op, group, n_cand, topk)
     if workspace is not None:
@@ -158,10 +183,11 @@ def score_topk(q, k, w, topk, q_scale=None, k_scale=None, q_pos0=None, return_sc
     With ``return_scores`` also returns the exact float32 [B, n_q, n_k] scores
     the select used (-inf beyond each query's prefix).
     """
+    B, n_q = q.shape[0], q.shape[1]
+    idx = _check_out(out, (B, n_q, topk), q)
+    _check_workspace_tensor(workspace, q)
     lib = load_library()
     p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
-    B, n_q = q.shape[0], q.shape[1]
-    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=q.device)
     scores = torch.empty((B, n_q, k.shape[1]), dtype=torch.float32, device=q.device) if return_scores else None
     ws = _workspace(p, IDX_OP_SCORE_TOPK, q.device, topk=topk, workspace=workspace)
     _check(lib.idx_score_topk(ctypes.byref(p), topk, _ptr(idx), _ptr(scores), _ptr(ws), ws.numel(),
@@ -176,6 +202,7 @@ def group_proxy_scan(q, k, w, group, n_cand, q_scale=None, k_scale=None, q_pos0=
     ``return_proxy`` adds the stored proxy (q as bfloat16, or float32 for
     float32 q; w float32); ``return_scores`` adds the proxy scores [B, n_g, n_k].
     """
+    _check_workspace_tensor(workspace, q)
     lib = load_library()
     p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
     B, n_q, H, d = q.shape
@@ -202,15 +229,17 @@ def group_proxy_scan(q, k, w, group, n_cand, q_scale=None, k_scale=None, q_pos0=
 def refine_topk(q, k, w, cand, group, topk, q_scale=None, k_scale=None, q_pos0=None,
                 return_scores=False, workspace=None, out=None):
     """PIVOT-Refine: int32 [B, n_q, topk]; optional per-candidate scores [B, n_q, n_cand]."""
-    lib = load_library()
-    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
     B, n_q = q.shape[0], q.shape[1]
     n_g = -(-n_q // group)
-    if cand.dtype != torch.int32 or cand.dim() != 3 or tuple(cand.shape[:2]) != (B, n_g):
-        raise IndexerError("cand must be int32 [B, n_g, n_cand]")
+    if not isinstance(cand, torch.Tensor) or cand.dtype != torch.int32 or cand.dim() != 3 \
+            or tuple(cand.shape[:2]) != (B, n_g) or not cand.is_contiguous():
+        raise IndexerError("cand must be a contiguous int32 tensor [B, n_g, n_cand]")
+    idx = _check_out(out, (B, n_q, topk), q)
+    _check_workspace_tensor(workspace, q)
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
     _need_gpu(cand)
     n_cand = cand.shape[2]
-    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=q.device)
     sc = torch.empty((B, n_q, n_cand), dtype=torch.float32, device=q.device) if return_scores else None
     ws = _workspace(p, IDX_OP_REFINE_TOPK, q.device, group, n_cand, topk, workspace=workspace)
     _check(lib.idx_refine_topk(ctypes.byref(p), group, _ptr(cand), n_cand, topk, _ptr(idx), _ptr(sc),
@@ -220,16 +249,17 @@ def refine_topk(q, k, w, cand, group, topk, q_scale=None, k_scale=None, q_pos0=N
 
 def reuse_topk(proxy_topk, group, n_q, n_k, q_pos0=None, out=None):
     """PIVOT-Reuse: int32 [B, n_q, topk] from the proxy top-k [B, n_g, topk]."""
-    lib = load_library()
-    if proxy_topk.dtype != torch.int32 or proxy_topk.dim() != 3:
-        raise IndexerError("proxy_topk must be int32 [B, n_g, topk]")
-    _need_gpu(proxy_topk)
+    if not isinstance(proxy_topk, torch.Tensor) or proxy_topk.dtype != torch.int32 or proxy_topk.dim() != 3 \
+            or not proxy_topk.is_contiguous():
+        raise IndexerError("proxy_topk must be a contiguous int32 tensor [B, n_g, topk]")
     B, n_g, topk = proxy_topk.shape
     if n_g != -(-n_q // group):
         raise IndexerError("proxy_topk has the wrong number of groups")
+    idx = _check_out(out, (B, n_q, topk), proxy_topk)
+    lib = load_library()
+    _need_gpu(proxy_topk)
     p = _Problem(B, n_q, n_k, n_k - n_q if q_pos0 is None else int(q_pos0), 0, 0, 0, 0,
                  None, None, None, None, None)
-    idx = out if out is not None else torch.empty((B, n_q, topk), dtype=torch.int32, device=proxy_topk.device)
     _check(lib.idx_reuse_topk(ctypes.byref(p), group, _ptr(proxy_topk), topk, _ptr(idx),
                               _stream(proxy_topk.device)))
     return idx
@@ -244,6 +274,7 @@ def block_route(q, k, w, group, block, n_sel, q_scale=None, k_scale=None, q_pos0
     [B, n_g, n_b] (-inf where a block is not routable); ``return_proxy`` adds
     the stored proxy q and w.
     """
+    _check_workspace_tensor(workspace, q)
     lib = load_library()
     p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
     B, n_q, H, d = q.shape
@@ -283,6 +314,7 @@ def ivf_build(k, n_clusters, refit, iters, k_scale=None, return_assign=False, wo
     ``assign`` [B, n_v, n_k] (-1 beyond it); plus the parameters.
     n_v = n_k // refit may be 0 (then the arrays are empty).
     """
+    _check_workspace_tensor(workspace, k)
     lib = load_library()
     if k.dim() != 3 or k.dtype not in _DTYPES:
         raise IndexerError("expected k [B, n_k, d] in float32, bfloat16 or float8_e4m3fn")
@@ -322,6 +354,7 @@ def ivf_route(q, k, w, index, group, insert_batch, n_cand, q_scale=None, k_scale
     ``return_scores`` adds the cluster scores [B, n_g, m] (-inf without a
     version); ``return_proxy`` adds the stored proxy q and w.
     """
+    _check_workspace_tensor(workspace, q)
     lib = load_library()
     p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
     B, n_q, H, d = q.shape

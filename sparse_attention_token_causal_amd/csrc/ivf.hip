@@ -4,11 +4,13 @@
 // "AttentionIndex Architecture ...", "KEY FINDINGS" and "An Inverted File
 // With Causal Versions": keys are grouped by similarity into inverted lists;
 // a query is routed to the lists whose representatives score highest and the
-// native indexer re-scores their members.  New keys are added to the lists in
-// small batches; periodic refits regroup the whole prefix starting from the
-// previous clustering and publish a new version (lists and representatives
-// together); a query uses a version only if every key that built it lies in
-// its prefix.  Here the representatives are plain means (no trained encoder):
+// native indexer re-scores their members.  The index grows with the keys:
+// arriving keys join existing lists batch by batch, and from time to time the
+// clustering is recomputed over all keys so far, seeded with the last one,
+// which yields a new version of lists and representatives.  Causality is kept
+// by version: a group may route through version u only when all of u's
+// keys precede its last member.  Here the representatives are plain means
+// (no trained encoder):
 //
 //  * version u is refit every R keys on keys [0, u R): T Lloyd iterations of
 //    k-means over the stored centroids (bfloat16, float32 for float32 keys),
