@@ -102,11 +102,8 @@ def make_step(S, wl, inp, dev):
                 it[0] += 1
             return step, dense_pairs, dense_pairs * 2 * H * d, wl.batch * wl.n_q, dtype, "decode"
         p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
-        # a workspace for every row at once (score rows, or candidate lists of
-        # (score, key) slots and a 16-byte record): one score and one select launch per step
-        ws_bytes = max(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk),
-                       wl.batch * wl.n_q * (wl.n_k * 8 + 16) + 4096)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        # exactly the workspace the library asks for
+        ws = torch.empty(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk), dtype=torch.uint8, device=dev)
         out = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device=dev)
 
         def step():

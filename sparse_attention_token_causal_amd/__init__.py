@@ -380,7 +380,7 @@ def ivf_route(q, k, w, index, group, insert_batch, n_cand, q_scale=None, k_scale
     return res[0] if len(res) == 1 else tuple(res)
 
 
-KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill", "ivf_build", "ivf_route")
+KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill", "ivf_build", "ivf_route", "rescan")
 
 
 def profile_enable(on=True):

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <vector>
 
 #include "kernels.hpp"
@@ -51,6 +52,10 @@ hipError_t timed(int kind, hipStream_t st, F launch) {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScoreBufferTarget = size_t(1) << 30;  // score rows buffered per chunk (bytes)
+// Candidate lists of a filtering dense scan buffered per chunk (bytes): the
+// workspace of idx_score_topk stays below this (plus a few bytes per row
+// block) at any sequence length.
+constexpr size_t kListBufferTarget = size_t(4) << 30;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -159,17 +164,31 @@ long long buffer_rows(const Layout& L, long long total_rows) {
 // per-row candidate lists in dense scans with one query per wave.
 struct Filter {
   bool on = false;
-  float* val = nullptr;   // [rows, n_k]
-  int* idx = nullptr;     // [rows, n_k]
-  int* count = nullptr;   // [rows]
+  int cap = 0;              // list capacity (entries per row)
+  float* val = nullptr;     // [rows, cap]
+  int* idx = nullptr;       // [rows, cap]
+  int* count = nullptr;     // [rows, kFiltInfoStride] records
+  int* ovf_cnt = nullptr;   // one overflow counter per chunk
+  int* ovf_list = nullptr;  // [blocks per chunk] overflowed row blocks of the current chunk
 };
 
 int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D, int B, int n_q,
                      int group, float* buf, long long buf_rows, bool full, int topk, int* out,
                      hipStream_t st, const Filter& flt = Filter()) {
-  const int bpc = full ? L.total_blocks : (int)(buf_rows / L.BQ);
-  if (bpc < 1) return IDX_EWORKSPACE;
+  const int bpc_max = full ? L.total_blocks : (int)(buf_rows / L.BQ);
+  if (bpc_max < 1) return IDX_EWORKSPACE;
+  // chunks of equal size (a short last chunk would run a launch of a few
+  // workgroups of the longest rows)
+  const int bpc = ceil_div(L.total_blocks, ceil_div(L.total_blocks, bpc_max));
   const int tw = (L.nw / L.rw) * 64;
+  if (flt.on) {
+    // the overflow counters of every chunk start at zero (a fill kernel: no
+    // memset, so that the call can be captured in a graph)
+    const int n_chunks = ceil_div(L.total_blocks, bpc);
+    if (timed(IDX_KERNEL_FILL, st, [&] { return launch_fill_i32(flt.ovf_cnt, (size_t)n_chunks, 0, st); }) !=
+        hipSuccess)
+      return IDX_EHIP;
+  }
   for (int blk0 = 0; blk0 < L.total_blocks; blk0 += bpc) {
     const int nb = (L.total_blocks - blk0 < bpc) ? L.total_blocks - blk0 : bpc;
     const long long r0 = block_start_row(L.mode, blk0, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
@@ -206,10 +225,21 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.cval = flt.val;
     sa.cidx = flt.idx;
     sa.ccount = flt.count;
-    sa.cld = L.n_cols;
+    sa.cld = flt.on ? flt.cap : L.n_cols;
     sa.topk = topk;
+    sa.ovf_count = flt.on ? flt.ovf_cnt + blk0 / bpc : nullptr;
+    sa.ovf_list = flt.ovf_list;
     if (timed(IDX_KERNEL_SCORE, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
       return IDX_EHIP;
+    if (flt.on) {
+      // rows whose candidates overflowed their list: a fixed grid of
+      // workgroups rescans the listed row blocks (none: it exits at once)
+      ScoreArgs rs = sa;
+      rs.filter = 2;
+      rs.n_blocks = std::min(nb, kRescanGrid);
+      if (timed(IDX_KERNEL_RESCAN, st, [&] { return launch_score(rs, qf, kf, H, D, 1, st); }) != hipSuccess)
+        return IDX_EHIP;
+    }
     SelectArgs se = {};
     se.scores = buf + (full ? r0 * (long long)L.n_cols : 0);
     se.ld = L.n_cols;
@@ -231,6 +261,8 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
       se.scores = flt.val;
       se.lidx = flt.idx;
       se.finfo = flt.count;
+      se.ld = flt.cap;
+      se.n_cols = flt.cap;
     }
     if (timed(IDX_KERNEL_SELECT, st, [&] { return launch_select(se, (int)(r1 - r0), st); }) != hipSuccess)
       return IDX_EHIP;
@@ -261,11 +293,58 @@ ScoreArgs base_args(const idx_problem* p) {
 // instead of writing full score rows.
 bool use_filter(const idx_problem* p, const Layout& L) { return L.filter && p->heads == 64; }
 
-// Workspace bytes per buffered row of a dense scan: a float score row, or a
-// candidate list (float score + int key per slot) and the scan's four-int
-// record for the select.
-size_t score_row_bytes(const idx_problem* p, const Layout& L) {
-  return use_filter(p, L) ? (size_t)p->n_k * 8 + 16 : (size_t)p->n_k * 4;
+// Entries a filtered candidate list holds.  A running top-k threshold over n
+// keys in random order admits about k (1 + ln(n / k)) of them, and every key
+// passes until the threshold first moves (at least topk keys, checked every
+// eight 64-key tiles).  On the 32K, 131K and 262K prefill workloads the
+// largest row held 8175, 11099 and 12569 candidates, at most 584 above that
+// estimate: the capacity is 1.25 times the estimate plus 1024 (28-31% above
+// those maxima), at least topk (a rescan cuts a tied class to exactly topk
+// entries) and at most n_k.  A row with more candidates is resolved exactly
+// by the rescan.
+int list_cap(int n_k, int topk) {
+  if (topk >= n_k) return n_k;
+  const double e = 1.25 * topk * (1.0 + std::log((double)n_k / topk)) + 1024.0;
+  long long c = ((long long)std::ceil(e) + 255) / 256 * 256;
+  if (c < topk) c = topk;
+  return (int)std::min<long long>(c, n_k);
+}
+
+// Workspace of a filtering dense scan: the overflow counters (one per chunk)
+// and the overflow list (one slot per row block), then for `rows` buffered
+// rows their lists ([rows, cap] scores, [rows, cap] keys) and records
+// ([rows, kFiltInfoStride] ints).
+struct FilterLayout {
+  int cap;
+  size_t row_bytes, fixed;
+  long long target_rows;  // rows the workspace buffers at the library's own size
+};
+
+FilterLayout filter_layout(const idx_problem* p, const Layout& L, int topk) {
+  FilterLayout F;
+  F.cap = list_cap(p->n_k, topk);
+  F.row_bytes = (size_t)F.cap * 8 + (size_t)kFiltInfoStride * 4;
+  F.fixed = 2 * align_up((size_t)L.total_blocks * 4);
+  long long rows = (long long)(kListBufferTarget / F.row_bytes) / L.BQ * L.BQ;
+  rows = std::max<long long>(rows, L.BQ);
+  rows = std::min<long long>(rows, (long long)L.total_blocks * L.BQ);
+  F.target_rows = rows;
+  return F;
+}
+
+// Carves a filtering scan's workspace; returns the rows it buffers (0: too small).
+long long carve_filter(const FilterLayout& F, const Layout& L, char* ws, size_t ws_bytes, Filter& flt) {
+  if (ws_bytes < F.fixed + (size_t)L.BQ * F.row_bytes) return 0;
+  const long long rows = (long long)((ws_bytes - F.fixed) / F.row_bytes);
+  flt.on = true;
+  flt.cap = F.cap;
+  flt.ovf_cnt = (int*)ws;
+  flt.ovf_list = (int*)(ws + F.fixed / 2);
+  char* lists = ws + F.fixed;
+  flt.val = (float*)lists;
+  flt.idx = (int*)(lists + (size_t)rows * F.cap * 4);
+  flt.count = (int*)(lists + (size_t)rows * F.cap * 8);
+  return rows;
 }
 
 size_t proxy_q_bytes(const idx_problem* p, int n_g) {
@@ -553,7 +632,12 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
   if (op == IDX_OP_SCORE_TOPK) {
     if (split_shape(p, p->n_q, p->q_dtype)) return split_layout(p, p->n_q).total;
     Layout L = make_layout(kModeDense, p, p->n_q, p->n_k, 1);
-    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * score_row_bytes(p, L));
+    if (use_filter(p, L)) {
+      if (topk < 1) return 0;
+      const FilterLayout F = filter_layout(p, L, topk);
+      return F.fixed + align_up((size_t)F.target_rows * F.row_bytes);
+    }
+    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * (size_t)p->n_k * 4);
   }
   if (group < 1) return 0;
   const int n_g = ceil_div(p->n_q, group);
@@ -613,16 +697,15 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
                             buf, rows, full, topk, out_idx, st);
   const size_t need = idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk);
   if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
-  rows = (long long)(ws_bytes / score_row_bytes(p, L));
-  if (!use_filter(p, L))
+  if (!use_filter(p, L)) {
+    rows = (long long)(ws_bytes / ((size_t)p->n_k * 4));
     return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
                             (float*)ws, rows, false, topk, out_idx, st);
-  // layout: [rows, n_k] float scores, [rows, n_k] int keys, [rows, 4] select records
+  }
+  // a larger workspace buffers more rows per chunk (fewer launches)
   Filter flt;
-  flt.on = true;
-  flt.val = (float*)ws;
-  flt.idx = (int*)((char*)ws + (size_t)rows * p->n_k * 4);
-  flt.count = (int*)((char*)ws + (size_t)rows * p->n_k * 8);
+  rows = carve_filter(filter_layout(p, L, topk), L, (char*)ws, ws_bytes, flt);
+  if (rows < L.BQ) return IDX_EWORKSPACE;
   return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
                           nullptr, rows, false, topk, out_idx, st, flt);
 }

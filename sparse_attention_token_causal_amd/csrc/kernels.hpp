@@ -32,11 +32,23 @@ __host__ __device__ inline int mode_limit(int mode, int q_pos0, int n_q, int gro
 // candidates, the histogram base (bin = clamp((order key >> 15) - base, 0,
 // 2047)), the boundary bin - the highest bin with at least topk candidates
 // at or above it (-2: fewer than topk candidates in all; -1: the boundary
-// bin holds more than kFiltBoundaryMax of them) - and the number of
-// candidates in bins above it.
+// bin holds more than kFiltBoundaryMax of them, or the list was rebuilt by
+// a rescan: the select's general path) - and the number of candidates in
+// bins above it.  A list holds at most `cld` entries; a row with more
+// candidates is pending (status 1) and its exact boundary interval is
+// narrowed by rescans: order keys above `hi` (there are exactly `A` of them,
+// A < topk) all win, the topk-th largest key lies in [lo, hi].
 constexpr int kFiltBins = 2048;  // filter histogram: 256 bins per octave of the score, 8 octaves
 constexpr int kFiltInfoCount = 0, kFiltInfoBase = 1, kFiltInfoBoundary = 2, kFiltInfoAbove = 3;
+constexpr int kFiltInfoStatus = 4, kFiltInfoLo = 5, kFiltInfoHi = 6, kFiltInfoA = 7;
+constexpr int kFiltInfoStride = 8;
 constexpr int kFiltBoundaryMax = 256;
+// Rescan levels that always resolve a pending row: 11-bit digits of the
+// order key (shifts 21, 10, 0), then one pass that keeps the lowest key
+// indices of an exactly tied class.
+constexpr int kRescanLevels = 4;
+// Workgroups of one rescan launch (they loop over the overflowed row blocks).
+constexpr int kRescanGrid = 256;
 
 struct ScoreArgs {
   const void* q;          // [B, n_rows, H, D] rows (queries or proxies)
@@ -61,15 +73,21 @@ struct ScoreArgs {
   // Candidate filtering (dense scans with one query per wave, whole rows per
   // workgroup): instead of full score rows, each row's candidates - every key
   // whose score reaches the row's running threshold bin - are written as
-  // (score, key) pairs at cval/cidx + (row - row0) * cld, and at
-  // ccount + 4 (row - row0) the row's record for the select (see
-  // kFiltInfo*): `topk` sets the threshold.
+  // (score, key) pairs at cval/cidx + (row - row0) * cld (at most cld of
+  // them), and at ccount + kFiltInfoStride (row - row0) the row's record for
+  // the select (see kFiltInfo*): `topk` sets the threshold.  filter = 1: the
+  // scan; a workgroup with a row of more than cld candidates appends its
+  // block id to ovf_list (ovf_count entries, zero before the scan).
+  // filter = 2: the rescan of those blocks (grid.x workgroups loop over the
+  // list; rows pending in their records are rescanned, the others skipped).
   int filter;
   float* cval;
   int* cidx;
   int* ccount;
   long long cld;
   int topk;
+  int* ovf_count;
+  int* ovf_list;
 };
 
 struct SelectArgs {
@@ -85,7 +103,7 @@ struct SelectArgs {
   const int* lidx;        // list: key indices, same layout as scores
   const int* counts;      // list: entries per launch row
   // filtered lists (when finfo is set; counts is then unused): launch row i's
-  // record finfo[4 i + kFiltInfo*] from the filtering scan
+  // record finfo[kFiltInfoStride i + kFiltInfo*] from the filtering scan
   const int* finfo;
   // segmented list (when seg_counts is set; counts is then unused): launch
   // row i holds seg_counts[i * n_segs + s] entries of segment s at

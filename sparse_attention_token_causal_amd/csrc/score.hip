@@ -106,7 +106,9 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // Filtering: bins of the running per-row histogram (256 per octave of the
 // score, a window of 8 octaves placed from the first tile's largest score).
 
-template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER>
+// FILTER: 0 full score rows; 1 the filtering scan (candidate lists); 2 the
+// rescan of the row blocks whose lists overflowed (see ScoreArgs::filter).
+template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, int FILTER>
 __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   constexpr int kScoreThreads = NWV * 64;  // threads of this workgroup
   typedef MfmaTraits<QF, KF> M;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // per-column data (key index, key scale) is only needed for gathered
   // columns or FP8 keys; dense scans of BF16/F32 keys use the position itself
   constexpr bool COLINFO = GATHER || KF == FP8;
-  static_assert(!FILTER || (!GATHER && QW == 1), "filtering: dense scans, one query per wave");
+  static_assert(FILTER == 0 || (!GATHER && QW == 1), "filtering: dense scans, one query per wave");
 
   // two tile buffers: [TW][ROWB] key rows, then TW column keys and TW scales
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -131,8 +133,33 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   const int rw = wave % RW, kw = wave / RW;
   constexpr int BQ = RW * QW;
 
+  // Rescan state of this wave's row (wave-uniform), kept in registers across
+  // the levels of one row block: the row is pending while its list cannot
+  // hold every key at or above the boundary interval [r_lo, r_hi]; r_A keys
+  // lie above it (all of them win) and the (topk - r_A)-th largest key of
+  // the interval is the row's last winner.
+  bool r_act = false;
+  uint32_t r_lo = 0u, r_hi = 0u;
+  int r_A = 0;
+
+  // Workgroup-wide "any" of a wave-uniform flag, through one int per wave
+  // after the filter histograms (the leading barrier retires the previous
+  // call's reads).
+  auto wg_any = [&](bool p) -> bool {
+    int* flags = (int*)(smem + 2 * TILE_BYTES + NW * kFiltBins * 4);
+    __syncthreads();
+    if (l == 0) flags[wave] = p ? 1 : 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) any |= flags[i];
+    return any != 0;
+  };
+
+  // The scan of one row block; the rescan (FILTER == 2) returns whether a
+  // row of the block is still pending after this level.
+  auto run = [&](const int bid, const int level) -> bool {
   // ---- which rows this workgroup owns (longest prefixes first) ----
-  const int bid = a.blk0 + (a.n_blocks - 1 - (int)blockIdx.x);
   int b, r_begin, r_end, g = 0;
   if (!GATHER) {
     const int bps = (a.n_rows + BQ - 1) / BQ;
@@ -147,15 +174,43 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     const int gs = g * a.group, ge = min(gs + a.group, a.n_q);
     r_begin = gs + (bid % bpg) * BQ;
     r_end = min(r_begin + BQ, ge);
-    if (r_begin >= r_end) return;
+    if (r_begin >= r_end) return false;
   }
   const int c_begin = (int)blockIdx.y * a.kc;
   int c_end = min(c_begin + a.kc, a.n_cols);
   if (!GATHER) c_end = min(c_end, row_limit(a, r_end - 1) + 1);
-  if (c_begin >= c_end) return;
+  if (c_begin >= c_end) return false;
+  const int t_first = r_begin + rw * QW;
+
+  // ---- the row's list, record and (rescan) state ----
+  long long crow = 0;
+  int* info = nullptr;
+  if constexpr (FILTER != 0) {
+    crow = (long long)b * a.n_rows + t_first - a.row0;
+    if (t_first < r_end) info = a.ccount + kFiltInfoStride * crow;
+  }
+  bool r_tie = false;
+  int r_need = 0, r_shift = 0;
+  if constexpr (FILTER == 2) {
+    if (level == 0) {
+      r_act = false;
+      if (info) {
+        r_act = __builtin_amdgcn_readfirstlane(info[kFiltInfoStatus]) != 0;
+        r_lo = (uint32_t)__builtin_amdgcn_readfirstlane(info[kFiltInfoLo]);
+        r_hi = (uint32_t)__builtin_amdgcn_readfirstlane(info[kFiltInfoHi]);
+        r_A = __builtin_amdgcn_readfirstlane(info[kFiltInfoA]);
+      }
+    }
+    // nothing pending in this block: the workgroup skips it (also the
+    // barrier that retires the previous block's LDS reads)
+    if (!wg_any(r_act)) return false;
+    r_tie = r_lo == r_hi;
+    r_need = a.topk - r_A;
+    // bins of the class histogram: 2048 over [r_lo, r_hi]
+    while (((r_hi - r_lo) >> r_shift) >= (uint32_t)kFiltBins) ++r_shift;
+  }
 
   // ---- resident q fragments and head weights of this wave's 64 rows ----
-  const int t_first = r_begin + rw * QW;
   typename M::frag afrag[2][NKS];
   float wreg[2][16];
 #pragma unroll
@@ -185,15 +240,17 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   }
 
   // ---- filtering state (one query per wave; wave-uniform) ----
+  // The scan counts every candidate (f_cnt) and stores the first cld of
+  // them; the rescan counts the interval's keys in `hist` (bins of
+  // 2^r_shift above r_lo) and, on a tied interval, c_cnt of its keys so far.
   uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES) + wave * kFiltBins;
-  int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0;
+  int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0, c_cnt = 0;
   float f_lo = neg_inf();  // lower edge of bin f_theta (-inf while f_theta == 0)
   bool f_based = false;
   float* f_val = nullptr;
   int* f_idx = nullptr;
-  if constexpr (FILTER) {
+  if constexpr (FILTER != 0) {
     for (int i = l; i < kFiltBins; i += kWave) hist[i] = 0;
-    const long long crow = (long long)b * a.n_rows + t_first - a.row0;
     f_val = a.cval + crow * a.cld;
     f_idx = a.cidx + crow * a.cld;
   }
@@ -353,8 +410,35 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       const bool mine = live && t < r_end && col < c_end;
       const bool ok = mine && key >= 0 && key <= qlim[qi];
       const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
-      if constexpr (!FILTER) {
+      if constexpr (FILTER == 0) {
         if (mine) a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
+      } else if constexpr (FILTER == 2) {
+        // Rescan: keys above the interval are always stored; the interval's
+        // keys are stored while they fit and counted in the class histogram,
+        // or, on an exactly tied interval, only the first r_need of them in
+        // key order (ties go to the lower index, and columns arrive in
+        // increasing order: tile by tile, lane by lane).
+        const uint32_t kv = ok ? order_key(val) : 0u;
+        const bool abv = r_act && ok && kv > r_hi;
+        const bool cls = r_act && ok && kv >= r_lo && kv <= r_hi;
+        const unsigned long long lt = (l == 0) ? 0ull : (~0ull >> (kWave - l));
+        bool wr = abv || cls;
+        if (r_tie) {
+          const unsigned long long cm = __ballot(cls);
+          wr = abv || (cls && c_cnt + __popcll(cm & lt) < r_need);
+          c_cnt += __popcll(cm);
+        } else if (cls) {
+          atomicAdd(&hist[(kv - r_lo) >> r_shift], 1u);
+        }
+        const unsigned long long pm = __ballot(wr);
+        if (wr) {
+          const int off = f_cnt + __popcll(pm & lt);
+          if (off < a.cld) {
+            f_val[off] = val;
+            f_idx[off] = key;
+          }
+        }
+        f_cnt += __popcll(pm);
       } else {
         // Running threshold: f_theta is a bin with at least topk counted
         // scores at or above it, so its lower edge f_lo bounds the row's final
@@ -378,8 +462,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
             atomicAdd(&hist[bin], 1u);
             const unsigned long long lt = (l == 0) ? 0ull : (~0ull >> (kWave - l));
             const int off = f_cnt + __popcll(pm & lt);
-            f_val[off] = val;
-            f_idx[off] = key;
+            if (off < a.cld) {  // beyond the list: counted, left to the rescan
+              f_val[off] = val;
+              f_idx[off] = key;
+            }
           }
         }
         const int np = __popcll(pm);
@@ -459,7 +545,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     mfma_block(bfB, buf, 1);
     partial(0, p0_prev);
     IDX_INTERLEAVE(1, false);
-    if constexpr (FILTER) {
+    if constexpr (FILTER == 1) {
       if ((((c0 - c_begin) / TW) & 7) == 7) advance_theta();
     }
     if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
@@ -475,37 +561,98 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   }
   partial(1, p1);
   epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, true);
-  if constexpr (FILTER) {
-    // The histogram counts every written candidate in its bin, so the bin
-    // where the count from the top reaches topk (and the count above it)
-    // is exact: the select then only ranks that bin's candidates.
-    int above = 0, bstar = -2, cnt_b = 0;
+  // The bin where the count from the top of `hist` reaches `need`: returns
+  // it (-2 when the histogram holds fewer), with the count in bins above it
+  // and in it.
+  auto boundary_bin = [&](int need, int& above, int& cnt_b) -> int {
+    above = 0;
+    cnt_b = 0;
     for (int hi = kFiltBins; hi > 0; hi -= kWave) {
       const int h = (int)hist[hi - 1 - l];  // lane j: bin hi - 1 - j (from the top)
       const int incl = wave_incl_scan(h);
-      const unsigned long long m = __ballot(above + incl >= a.topk);
+      const unsigned long long m = __ballot(above + incl >= need);
       if (m) {
         const int J = __builtin_ctzll(m);
         const int hJ = __shfl(h, J, kWave), iJ = __shfl(incl, J, kWave);
-        bstar = hi - 1 - J;
         cnt_b = hJ;
         above += iJ - hJ;
-        break;
+        return hi - 1 - J;
       }
       above += __shfl(incl, kWave - 1, kWave);
     }
+    return -2;
+  };
+  if constexpr (FILTER == 1) {
+    // The histogram counts every candidate in its bin, so the bin where the
+    // count from the top reaches topk (and the count above it) is exact:
+    // the select then only ranks that bin's candidates.  A row with more
+    // candidates than its list holds is left pending for the rescan, which
+    // starts from the whole key range.
+    int above, cnt_b;
+    const int bstar = boundary_bin(a.topk, above, cnt_b);
+    const bool ovf = t_first < r_end && f_cnt > a.cld;
     if (l == 0 && t_first < r_end) {
-      int* info = a.ccount + 4 * ((long long)b * a.n_rows + t_first - a.row0);
       info[kFiltInfoCount] = f_cnt;
       info[kFiltInfoBase] = f_base;
-      info[kFiltInfoBoundary] = (bstar == -2 || cnt_b <= kFiltBoundaryMax) ? bstar : -1;
+      info[kFiltInfoBoundary] = (!ovf && (bstar == -2 || cnt_b <= kFiltBoundaryMax)) ? bstar : -1;
       info[kFiltInfoAbove] = above;
+      info[kFiltInfoStatus] = ovf ? 1 : 0;
+      info[kFiltInfoLo] = 1;            // every eligible order key is >= 1
+      info[kFiltInfoHi] = (int)0xFFFFFFFFu;
+      info[kFiltInfoA] = 0;
     }
+    if (wg_any(ovf) && threadIdx.x == 0) {
+      const int j = atomicAdd(a.ovf_count, 1);
+      a.ovf_list[j] = bid;
+    }
+  }
+  if constexpr (FILTER == 2) {
+    bool pend = false;
+    int d = 0, above = 0, cnt_b = 0;
+    // narrow the interval to the bin of its r_need-th largest key (the
+    // interval holds at least r_need keys: d >= 0 whenever f_cnt > cld)
+    if (r_act && !r_tie && f_cnt > a.cld) d = boundary_bin(r_need, above, cnt_b);
+    if (r_act) {
+      if (r_tie || f_cnt <= a.cld || d < 0) {
+        // every key at or above the interval is stored (on a tied interval
+        // exactly topk of them): the select's general path ranks the list
+        if (l == 0) {
+          info[kFiltInfoCount] = min(f_cnt, (int)a.cld);
+          info[kFiltInfoBoundary] = -1;
+          info[kFiltInfoAbove] = 0;
+          info[kFiltInfoStatus] = 0;
+        }
+        r_act = false;
+      } else {
+        r_lo += (uint32_t)d << r_shift;
+        // the bin's last key, saturated at the top of the key range
+        const unsigned long long top = (unsigned long long)r_lo + ((1ull << r_shift) - 1ull);
+        r_hi = top < (unsigned long long)r_hi ? (uint32_t)top : r_hi;
+        r_A += above;
+        pend = true;
+      }
+    }
+    return wg_any(pend);
+  }
+  return false;
+  };  // run
+
+  if constexpr (FILTER == 2) {
+    // the overflowed row blocks of this launch's chunk, each rescanned until
+    // all its rows are resolved (at most kRescanLevels levels)
+    const int n_over = *a.ovf_count;
+    for (int j = (int)blockIdx.x; j < n_over; j += (int)gridDim.x) {
+      const int bid = a.ovf_list[j];
+      for (int level = 0; level < kRescanLevels; ++level)
+        if (!run(bid, level)) break;
+    }
+  } else {
+    run(a.blk0 + (a.n_blocks - 1 - (int)blockIdx.x), 0);
   }
 #undef IDX_INTERLEAVE
 }
 
-template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, bool FILTER = false>
+template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, int FILTER = 0>
 static hipError_t launch_mode(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   static bool attr_set = false;  // once per instantiation: allow more than 64 KiB of LDS
   if (!attr_set) {
@@ -523,7 +670,8 @@ template <int QF, int KF, int H, int D, int RW>
 static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStream_t st) {
   const bool g = a.mode == kModeGather;
   if constexpr (H == 64 && RW == 8) {
-    if (a.filter && !g) return launch_mode<QF, KF, H, D, 8, false, 8, true>(a, grid, lds, st);
+    if (a.filter == 1 && !g) return launch_mode<QF, KF, H, D, 8, false, 8, 1>(a, grid, lds, st);
+    if (a.filter == 2 && !g) return launch_mode<QF, KF, H, D, 8, false, 8, 2>(a, grid, lds, st);
   }
   if (RW == 4 && a.nw == 4)
     return g ? launch_mode<QF, KF, H, D, 4, true, 4>(a, grid, lds, st)
@@ -559,10 +707,10 @@ size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int ga
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
   const int tw = (nw / rw) * 64;
   (void)kf;
-  // double-buffered tiles, then one filtering histogram per wave (dense
-  // scans) or the workgroup's candidate key indices (gather)
+  // double-buffered tiles, then one filtering histogram and one flag per
+  // wave (dense scans) or the workgroup's candidate key indices (gather)
   return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) +
-         (filter ? (size_t)nw * kFiltBins * 4 : 0) + (size_t)gather_cols * 4;
+         (filter ? (size_t)nw * (kFiltBins * 4 + 4) : 0) + (size_t)gather_cols * 4;
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,

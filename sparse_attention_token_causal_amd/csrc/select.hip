@@ -51,7 +51,8 @@ struct SelectShared {
 
 __device__ __forceinline__ int row_length(const SelectArgs& a, int r) {
   if (a.mode == kModeList)
-    return min(a.finfo ? a.finfo[4 * (long long)blockIdx.x + kFiltInfoCount] : a.counts[blockIdx.x], a.n_cols);
+    return min(a.finfo ? a.finfo[kFiltInfoStride * (long long)blockIdx.x + kFiltInfoCount] : a.counts[blockIdx.x],
+               a.n_cols);
   if (a.mode == kModeGather) return a.n_cols;
   const int lim = mode_limit(a.mode, a.q_pos0, a.n_q, a.group, a.block, r);
   return min(lim + 1, a.n_cols);
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
     // candidate above the boundary bin (there are exactly `above` of them),
     // collects the boundary bin's candidates (at most kFiltBoundaryMax), and
     // those are ranked exactly by (score descending, key ascending).
-    const int* fi = a.finfo + 4 * (long long)blockIdx.x;
+    const int* fi = a.finfo + kFiltInfoStride * (long long)blockIdx.x;
     const int bstar = fi[kFiltInfoBoundary];
     if (bstar != -1) {
       const int n = min(fi[kFiltInfoCount], a.n_cols), base = fi[kFiltInfoBase];

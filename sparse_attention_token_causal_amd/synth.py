@@ -23,7 +23,10 @@ Two further structures exist only to exercise the select's tie handling:
 small-integer queries, keys and weights ("int": values in {-2..2}, weights
 in {0, 1, 2}), where many scores are exactly equal, and identical keys
 ("const": every key row is the same N(0,1) vector), where every score of a
-query ties.
+query ties.  A third exists to defeat a running top-k threshold: "ramp"
+keys k_s = (s + 1) / n_k * |v| for one N(0,1) vector v, so that every
+query's scores grow with the key position (up to storage rounding) and
+nearly every key beats the best ones seen before it.
 
 Draw order per call: query noise, keys, heavy-row choice, weights, all from
 one torch generator seeded with ``seed`` on the target device.
@@ -48,7 +51,7 @@ class Workload:
     q_fmt: str          # "f32" | "bf16" | "fp8"
     k_fmt: str
     q_dist: str         # "normal8" | "ar1" | "int"
-    k_dist: str         # "normal8" | "heavy" | "int" | "const"
+    k_dist: str         # "normal8" | "heavy" | "int" | "const" | "ramp" | "clustered"
     rho: float = 0.0
     topk: int = 2048
     group: int = 0      # 0: dense only
@@ -139,6 +142,9 @@ def make_inputs(wl: Workload, device="cpu"):
         k = torch.clamp(torch.round(k * 1.5), -2, 2)
     elif wl.k_dist == "const":
         k = k[:, :1].expand(B, nk, d).clone()
+    elif wl.k_dist == "ramp":
+        ramp = torch.arange(1, nk + 1, device=device, dtype=torch.float32).reshape(1, nk, 1) / nk
+        k = ramp * k[:, :1].abs()
     elif wl.k_dist == "heavy":
         n_heavy = nk // 100
         for b in range(B):

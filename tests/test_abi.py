@@ -173,12 +173,17 @@ def test_workspace_sizes_follow_the_layout(lib):
     p = problem(n_q=1000, n_k=1000)
     need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 8)
     assert need >= 1000 * 1000 * 4 and need % 256 == 0
-    # large: about 1 GiB-worth of buffered score rows; with 64 heads the rows
-    # are candidate lists (score + key per slot, plus a 16-byte record): twice that
+    # large, 64 heads: candidate lists of cap = 1.25 k (1 + ln(n / k)) + 1024 entries
+    # (rounded up to 256) of a score and a key each, plus a 32-byte record, for
+    # whole 8-row blocks within a 4 GiB budget, after two int slots per row block
+    import math
     big = problem(n_q=131072, n_k=131072)
     nb = lib.idx_workspace_bytes(ctypes.byref(big), 0, 0, 0, 2048)
-    rows = (1 << 30) // (131072 * 4)
-    assert nb >= rows * (131072 * 8 + 16) and nb <= (rows + 8) * (131072 * 8 + 16) + 256
+    cap = -(-math.ceil(1.25 * 2048 * (1 + math.log(131072 / 2048)) + 1024) // 256) * 256
+    row = cap * 8 + 32
+    rows = (4 << 30) // row // 8 * 8
+    fixed = 2 * (-(-(131072 // 8) * 4 // 256) * 256)
+    assert fixed + rows * row <= nb <= fixed + rows * row + 256
     big32 = problem(n_q=131072, n_k=131072, heads=32)
     nb32 = lib.idx_workspace_bytes(ctypes.byref(big32), 0, 0, 0, 2048)
     assert (1 << 30) <= nb32 <= (1 << 30) + 16 * 131072 * 4 + 256
@@ -215,3 +220,29 @@ def test_calibration_recall_matches_the_oracle_definition():
             dict(path="b", recall_mean=0.99, ms=5.0), dict(path="c", recall_mean=0.80, ms=1.0)]
     assert choose(rows, 0.9)["path"] == "a" and choose(rows, 0.98)["path"] == "b"
     assert choose(rows, 0.999) is None
+
+
+def test_dense_workspace_is_bounded_at_any_length(lib):
+    """The dense scan's candidate lists hold a bounded number of entries per row
+    (about 1.25 k (1 + ln(n / k))), and the workspace buffers whole row blocks up to
+    a fixed budget: its size stops growing with the sequence length (beyond a
+    few bytes per row block for the overflow bookkeeping)."""
+    sizes = {}
+    for n in (32768, 131072, 262144, 1 << 20):
+        p = problem(n_q=n, n_k=n)
+        sizes[n] = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 2048)
+    budget = (4 << 30) + 2 * ((1 << 20) // 8) * 4 + 4096
+    for n, b in sizes.items():
+        assert 0 < b <= budget, (n, b)
+    # far below one float per (query, key) pair: 4 n^2 bytes would be 4 GiB at 32K, 4 TiB at 1M
+    assert sizes[1 << 20] < sizes[32768] * 2
+    # decode shapes (at most four queries per sequence) take the split-key scan
+    p = problem(batch=8, n_q=2, n_k=131072, q_pos0=131070, k_dtype=2, k_scale=FAKE)
+    assert 0 < lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 2048) < (64 << 20)
+
+
+def test_short_workspace_is_refused(lib):
+    p = problem(n_q=4096, n_k=4096)
+    need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 256)
+    assert need > 0
+    assert score(lib, p, topk=256, ws=FAKE, ws_bytes=need - 1) == -3

@@ -45,6 +45,18 @@ DENSE = [
              rho=0.98, topk=150, seed=13, w_dist="signed"),
     Workload("filter_fp8_B2_L900_H64_k64", 2, 900, 900, 64, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99,
              topk=64, seed=14),
+    # rows with more candidates than their list holds (scores growing along
+    # the key axis; every score of a query tied): the overflowed row blocks
+    # are rescanned, narrowing the boundary interval digit by digit, and a
+    # tied class is cut to its lowest key indices
+    Workload("filter_overflow_ramp_H64_L6000_k100", 1, 6000, 6000, 64, 128, "bf16", "bf16", "normal8", "ramp",
+             topk=100, seed=21),
+    Workload("filter_overflow_ramp_fp8_B2_L4000_k64", 2, 4000, 4000, 64, 128, "fp8", "fp8", "ar1", "ramp",
+             rho=0.99, topk=64, seed=22),
+    Workload("filter_overflow_tied_H64_L5000_k300", 1, 5000, 5000, 64, 128, "bf16", "bf16", "normal8", "const",
+             topk=300, seed=23),
+    Workload("filter_overflow_int_H64_L4500_k40", 1, 4500, 4500, 64, 64, "bf16", "bf16", "int", "int",
+             topk=40, seed=24, w_dist="int"),
     # at most 4 rows per sequence take the split-key scan + histogram compaction:
     # fp8 x fp8 with a partly empty row-wave, d = 64, ties, k near the prefix
     Workload("split_fp8_B2_nq3_H32_d128", 2, 3, 4099, 32, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99,
