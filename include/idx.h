@@ -72,7 +72,8 @@ enum {
   IDX_EINVAL = -1,
   IDX_EUNSUPPORTED = -2,
   IDX_EWORKSPACE = -3,
-  IDX_EHIP = -4
+  IDX_EHIP = -4,
+  IDX_ETOOLARGE = -5  /* beyond the fixed scratch of idx_score_topk_static */
 };
 
 /* Operation codes for idx_workspace_bytes. */
@@ -128,6 +129,24 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group,
  * 0, 0, topk) bytes (may be NULL when that is 0). */
 int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx,
                        float* out_scores, void* ws, size_t ws_bytes, void* stream);
+
+/* idx_score_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * (the decode step), harnesses that forbid allocation.  Same computation,
+ * arguments, layouts and errors as idx_score_topk; its scratch is a fixed
+ * device array of IDX_STATIC_SCRATCH_BYTES (64 MiB) that each GPU the library
+ * runs on holds until the process ends (its address is resolved on the first
+ * call on a device).  Returns IDX_ETOOLARGE, before enqueueing anything, when
+ * idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk) exceeds that size
+ * (decode shapes fit: 8 sequences x 2 queries x 131072 keys need about
+ * 41 MiB).  Calls no allocating routine.  Every call on one GPU shares the
+ * array, which keeps the last call's contents (nothing in it needs to start
+ * at zero): calls that overlap in time on one GPU - on different streams or
+ * from different host threads without ordering - race and corrupt each
+ * other's results; order them on one stream. */
+#define IDX_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t idx_score_topk_static(const idx_problem* p, int32_t topk, int32_t* out_idx, float* out_scores,
+                              void* stream);
 
 /* PIVOT proxy and shared scan (PIVOT, Abstract: aggregate a group into one
  * proxy query and run one shared full-prefix scan to a candidate set).

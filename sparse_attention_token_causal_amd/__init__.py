@@ -10,6 +10,7 @@ the functions raise if the library has not been built.
 Entry points (same names as the C ABI):
 
 * ``score_topk``        dense causal scan + per-query top-k
+* ``score_topk_static`` the same without allocating (fixed device scratch)
 * ``group_proxy_scan``  PIVOT proxy per group + one shared prefix scan -> candidates
 * ``refine_topk``       PIVOT-Refine: per-query re-score of the group's candidates
 * ``reuse_topk``        PIVOT-Reuse: the group's shared top-k, causally filtered
@@ -73,6 +74,8 @@ def load_library():
         lib.idx_workspace_bytes.argtypes = [P, i32, i32, i32, i32]
         lib.idx_score_topk.restype = i32
         lib.idx_score_topk.argtypes = [P, i32, vp, vp, vp, sz, vp]
+        lib.idx_score_topk_static.restype = i32
+        lib.idx_score_topk_static.argtypes = [P, i32, vp, vp, vp]
         lib.idx_group_proxy_scan.restype = i32
         lib.idx_group_proxy_scan.argtypes = [P, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         lib.idx_refine_topk.restype = i32
@@ -193,6 +196,19 @@ def score_topk(q, k, w, topk, q_scale=None, k_scale=None, q_pos0=None, return_sc
     _check(lib.idx_score_topk(ctypes.byref(p), topk, _ptr(idx), _ptr(scores), _ptr(ws), ws.numel(),
                               _stream(q.device)))
     return (idx, scores) if return_scores else idx
+
+
+def score_topk_static(q, k, w, topk, q_scale=None, k_scale=None, q_pos0=None, out=None):
+    """``score_topk`` through the entry point that allocates nothing on the
+    device (its scratch is the library's fixed 64 MiB device array; see
+    idx_score_topk_static).  ``out`` may be given so that nothing is
+    allocated here either."""
+    B, n_q = q.shape[0], q.shape[1]
+    idx = _check_out(out, (B, n_q, topk), q)
+    lib = load_library()
+    p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
+    _check(lib.idx_score_topk_static(ctypes.byref(p), topk, _ptr(idx), None, _stream(q.device)))
+    return idx
 
 
 def group_proxy_scan(q, k, w, group, n_cand, q_scale=None, k_scale=None, q_pos0=None,
@@ -397,6 +413,6 @@ def profile_read():
     return {KERNEL_KINDS[i]: (float(ms[i]), int(cnt[i])) for i in range(n)}
 
 
-__all__ = ["profile_enable", "profile_read", "score_topk", "group_proxy_scan", "refine_topk", "reuse_topk",
+__all__ = ["profile_enable", "profile_read", "score_topk", "score_topk_static", "group_proxy_scan", "refine_topk", "reuse_topk",
            "block_route", "ivf_build", "ivf_route", "make_problem",
            "workspace_bytes", "load_library", "library_path", "IndexerError"]

@@ -616,6 +616,7 @@ const char* idx_status_string(int32_t s) {
     case IDX_EUNSUPPORTED: return "unsupported heads/dim/dtype combination";
     case IDX_EWORKSPACE: return "workspace too small";
     case IDX_EHIP: return "HIP launch error";
+    case IDX_ETOOLARGE: return "problem needs more scratch than the fixed device array of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -708,6 +709,18 @@ int32_t idx_score_topk(const idx_problem* p, int32_t topk, int32_t* out_idx, flo
   if (rows < L.BQ) return IDX_EWORKSPACE;
   return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q, 1,
                           nullptr, rows, false, topk, out_idx, st, flt);
+}
+
+int32_t idx_score_topk_static(const idx_problem* p, int32_t topk, int32_t* out_idx, float* out_scores,
+                              void* stream) {
+  static_assert(IDX_STATIC_SCRATCH_BYTES == kStaticScratchBytes, "header and library scratch sizes agree");
+  int rc = check_problem(p);
+  if (rc != IDX_OK) return rc;
+  if (topk < 1 || !out_idx) return IDX_EINVAL;
+  if (idx_workspace_bytes(p, IDX_OP_SCORE_TOPK, 0, 0, topk) > kStaticScratchBytes) return IDX_ETOOLARGE;
+  void* scratch = nullptr;
+  if (static_scratch_ptr(&scratch) != hipSuccess) return IDX_EHIP;
+  return idx_score_topk(p, topk, out_idx, out_scores, scratch, kStaticScratchBytes, stream);
 }
 
 int32_t idx_group_proxy_scan(const idx_problem* p, int32_t group, int32_t n_cand,

@@ -268,6 +268,11 @@ struct IvfRouteArgs {
 };
 
 hipError_t launch_fill_i32(int* p, size_t n, int v, hipStream_t st);
+
+// The fixed device scratch of the no-allocation entry point (see
+// static_scratch.hip): its size, and its address on the current device.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+hipError_t static_scratch_ptr(void** out);
 hipError_t launch_ivf_init(const void* k, const float* k_scale, int kf, int B, int n_k, int D, int m, int R,
                            void* dst, long long dst_bs, hipStream_t st);
 hipError_t launch_ivf_pass(const IvfPassArgs& a, int kf, int D, int B, hipStream_t st);

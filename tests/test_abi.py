@@ -246,3 +246,14 @@ def test_short_workspace_is_refused(lib):
     need = lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 256)
     assert need > 0
     assert score(lib, p, topk=256, ws=FAKE, ws_bytes=need - 1) == -3
+
+
+def test_static_entry_point_refuses_problems_beyond_its_scratch(lib):
+    """idx_score_topk_static checks its fixed 64 MiB scratch on the host: a
+    32K-token prefill needs far more and is refused before anything runs."""
+    p = problem(n_q=32768, n_k=32768)
+    assert lib.idx_workspace_bytes(ctypes.byref(p), 0, 0, 0, 2048) > (64 << 20)
+    assert lib.idx_score_topk_static(ctypes.byref(p), 2048, FAKE, None, None) == -5
+    assert b"fixed" in lib.idx_status_string(-5)
+    assert lib.idx_score_topk_static(ctypes.byref(problem(n_q=0)), 8, FAKE, None, None) == -1
+    assert lib.idx_score_topk_static(ctypes.byref(problem()), 0, FAKE, None, None) == -1
