@@ -1,18 +1,29 @@
 #!/usr/bin/env python3
-"""Throughput of the causal lightning indexer on one MI355X.
+"""Throughput of the causal lightning indexer and its group-shared (PIVOT) variant on one MI355X.
 
-One step = one call of the hot path on one batch of synthetic input that is
-already resident in HBM.  The default workload is the dense causal scan +
-per-query top-k at L = 32768, 64 heads, d = 128, bfloat16 q/k, k = 2048
-(``prefill_bf16_L32768_H64_d128_k2048``); other workloads (decode, PIVOT
-grouped) can be selected with --workload.
+By default every specified workload runs in this one process and ONE JSON
+line is printed.  Its headline is the largest single-GPU workload: PIVOT-Refine
+at L = 262144 with FP8 queries and keys (groups of 128 consecutive queries, a
+shared proxy scan to 8192 candidates, each member's own re-score and top-2048),
+one step = proxy build + proxy scan + candidate select + gathered re-score +
+per-query select ("PIVOT: Efficient Query-Group Indexing for Token-Level
+Sparse Attention", Abstract).  The same workload's dense scan (the full-scan
+baseline on the same inputs) and PIVOT-Reuse are timed beside it as legs, and
+the other four workloads (the 1024-token float32 and 32K-token bfloat16 dense
+prefills, the 8 x 2 decode step over 131072 FP8 keys with its decode grouping,
+and PIVOT-Refine at 131072 bfloat16 tokens) follow as sub-records.
 
-Prints one JSON line: pairs scored per second (all heads of a causal
-(query, key) pair count once), top-k queries per second, the score kernel's
-achieved MFMA rate against the bf16/fp8 dense peak (per-launch HIP events
-recorded by the library on the launch stream, in a second run of the same
-steps so that the events stay out of the step time), and the CPU oracle timed
-on a bounded sample of the same workload on this host's cores.
+For every leg: milliseconds per step (wall clock over the timed steps, inputs
+resident in HBM), pairs scored per second (all heads of a causal (query, key)
+pair count once; a grouped leg counts the pairs it actually scores - proxy
+plus re-score - and also reports dense pairs divided by its time), top-k
+queries per second, the per-kernel times of the same steps (HIP events the
+library records on the launch stream, in a second run so that the events stay
+out of the step time), the roofline of the leg's dominant kernel against that
+kernel's own peak (MFMA for prefill scans at the dtype the MFMAs run in; HBM
+for the decode scans), and for grouped legs the speedup over the dense leg
+and the recall of the dense top-k over every query.  The CPU oracle is timed
+on a bounded sample of each workload on this host.
 """
 
 import argparse
@@ -27,17 +38,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "indexer query·key pairs scored/sec + top-k queries/sec; %MFMA / %HBM peak"
-DEFAULT_WORKLOAD = "prefill_bf16_L32768_H64_d128_k2048"
+HEADLINE = "grouped_fp8_L262144_G128_C8192_k2048"
+ORDER = ["prefill_f32_L1024_H16_d64_k128", "prefill_bf16_L32768_H64_d128_k2048",
+         "decode_fp8k_B8_mtp2_n131072_H64_d128_k2048", "grouped_refine_bf16_L131072_G64_C8192_k2048",
+         HEADLINE]
 
 # MI355X published dense peaks (no sparsity), TFLOP/s, and HBM3E GB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 
-# sources of the scan kernels whose HBM traffic the committed PMC runs measured
+# sources of the kernels whose HBM traffic the committed PMC runs measured,
+# and of the launcher that sets their launch shapes (chunking, grids)
 KERNEL_SOURCES = ["sparse_attention_token_causal_amd/csrc/score.hip",
                   "sparse_attention_token_causal_amd/csrc/split.hip",
                   "sparse_attention_token_causal_amd/csrc/common.hpp",
-                  "sparse_attention_token_causal_amd/csrc/kernels.hpp"]
+                  "sparse_attention_token_causal_amd/csrc/kernels.hpp",
+                  "sparse_attention_token_causal_amd/csrc/api.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "kernel_traffic.json")
 
 
@@ -45,13 +61,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def causal_pairs(n_q, n_k, q_pos0, limits=None):
-    """Sum over rows of (limit + 1) keys; limits default to q_pos0 + t."""
-    if limits is None:
-        first = q_pos0 + 1
-        last = q_pos0 + n_q
-        return (first + last) * n_q // 2
-    return int(sum(int(x) + 1 for x in limits))
+def causal_pairs(n_q, q_pos0):
+    """Causal (query, key) pairs of one sequence: sum over t of pos(t) + 1."""
+    first, last = q_pos0 + 1, q_pos0 + n_q
+    return (first + last) * n_q // 2
+
+
+def group_limits(wl, G):
+    n_g = -(-wl.n_q // G)
+    return [wl.q_pos0 + min((g + 1) * G, wl.n_q) - 1 for g in range(n_g)]
 
 
 def kernel_source_hash():
@@ -62,12 +80,12 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per scan launch from committed rocprofv3 PMC runs ({workload:
-    record}), if they were taken on the current kernel sources; else None."""
+def measured_traffic(workload, leg):
+    """HBM bytes per launch of a leg's dominant kernel from committed rocprofv3
+    PMC runs, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(workload)
+            rec = json.load(f).get(f"{workload}/{leg}")
     except (OSError, ValueError, AttributeError):
         return None
     if not rec or rec.get("kernel_source_sha") != kernel_source_hash():
@@ -75,80 +93,18 @@ def measured_traffic(workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def make_step(S, wl, inp, dev):
-    """Returns (step(), pairs_per_step, flops_per_step, queries_per_step, dtype, kind)."""
-    import torch
-    from sparse_attention_token_causal_amd.synth import make_inputs
-
-    H, d = wl.heads, wl.dim
-    a = dict(q_scale=inp["q_scale"], k_scale=inp["k_scale"], q_pos0=wl.q_pos0)
-    dense_pairs = wl.batch * causal_pairs(wl.n_q, wl.n_k, wl.q_pos0)
-    dtype = "fp8" if wl.q_fmt == "fp8" else ("f32" if wl.q_fmt == "f32" else "bf16")
-    if wl.group == 0 or wl.name.startswith("decode") or wl.name.startswith("prefill"):
-        if wl.n_q < wl.n_k:
-            # decode: the key cache (134 MB) fits the 256 MB Infinity Cache, so the
-            # steps rotate over four independent caches (>= 540 MB) to time HBM reads
-            sets = [inp] + [make_inputs(wl.scaled(seed=wl.seed + i), dev) for i in range(1, 4)]
-            outs = [torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device=dev) for _ in sets]
-            p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
-            ws = torch.empty(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk), dtype=torch.uint8,
-                             device=dev)
-            it = [0]
-
-            def step():
-                x = sets[it[0] % len(sets)]
-                S.score_topk(x["q"], x["k"], x["w"], wl.topk, q_scale=x["q_scale"], k_scale=x["k_scale"],
-                             q_pos0=wl.q_pos0, workspace=ws, out=outs[it[0] % len(sets)])
-                it[0] += 1
-            return step, dense_pairs, dense_pairs * 2 * H * d, wl.batch * wl.n_q, dtype, "decode"
-        p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
-        # exactly the workspace the library asks for
-        ws = torch.empty(S.workspace_bytes(p, S.IDX_OP_SCORE_TOPK, topk=wl.topk), dtype=torch.uint8, device=dev)
-        out = torch.empty((wl.batch, wl.n_q, wl.topk), dtype=torch.int32, device=dev)
-
-        def step():
-            S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, workspace=ws, out=out, **a)
-        return step, dense_pairs, dense_pairs * 2 * H * d, wl.batch * wl.n_q, dtype, "dense"
-
-    # PIVOT grouped: one proxy scan to C candidates, then each member's Refine
-    import numpy as np
-    G, C, K = wl.group, wl.n_cand, wl.topk
-    n_g = -(-wl.n_q // G)
-    lim = [wl.q_pos0 + min((g + 1) * G, wl.n_q) - 1 for g in range(n_g)]
-    proxy_pairs = wl.batch * causal_pairs(n_g, wl.n_k, 0, lim)
-    refine_pairs = wl.batch * sum(min(G, wl.n_q - g * G) * min(C, lim[g] + 1) for g in range(n_g))
-    p = S.make_problem(inp["q"], inp["k"], inp["w"], **a)
-    ws_p = torch.empty(S.workspace_bytes(p, S.IDX_OP_GROUP_PROXY_SCAN, G, C), dtype=torch.uint8, device=dev)
-    ws_r = torch.empty(max(S.workspace_bytes(p, S.IDX_OP_REFINE_TOPK, G, C, K),
-                           wl.batch * wl.n_q * C * 4), dtype=torch.uint8, device=dev)
-    out = torch.empty((wl.batch, wl.n_q, K), dtype=torch.int32, device=dev)
-
-    def step():
-        cand = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], G, C, workspace=ws_p, **a)
-        S.refine_topk(inp["q"], inp["k"], inp["w"], cand, G, K, workspace=ws_r, out=out, **a)
-    pairs = proxy_pairs + refine_pairs
-    return step, pairs, pairs * 2 * H * d, wl.batch * wl.n_q, dtype, "refine"
-
-
-def cpu_baseline(wl, inp, seconds):
-    """The oracle as it stands, on evenly spaced queries of the same inputs,
-    sequence after sequence, until about `seconds` of CPU work or the whole
-    workload (the decode workloads are small); returns the JSON object."""
-    import numpy as np
-    import oracle as O
-    from sparse_attention_token_causal_amd import synth
-
+def blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads = len(os.sched_getaffinity(0))
-    n = wl.n_q
-    order = []
-    # evenly spaced queries, refined by bisection so any prefix of the list is spread out
-    step = n
-    seen = set()
-    while step >= 1 and len(order) < n:
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        return None
+
+
+def spread_order(n):
+    """0..n-1 ordered so that every prefix is spread evenly (bisection), last element first."""
+    order, seen, step = [n - 1], {n - 1}, n
+    while step >= 1:
         for t in range(step // 2 if step > 1 else 0, n, max(step, 1)):
             if t not in seen:
                 seen.add(t)
@@ -156,44 +112,300 @@ def cpu_baseline(wl, inp, seconds):
         if step == 1:
             break
         step //= 2
-    pairs = 0
-    done = 0
+    return order
+
+
+# ----------------------------------------------------------------------------
+# legs: each returns a callable step and what one step computes
+
+
+class Leg:
+    def __init__(self, name, step, pairs, queries, kernel, bound, dtype, flops=0.0, hbm_bytes=0.0):
+        self.name, self.step, self.pairs, self.queries = name, step, pairs, queries
+        self.kernel, self.bound, self.dtype = kernel, bound, dtype
+        self.flops, self.hbm_bytes = flops, hbm_bytes
+        self.out = None  # the output of the last step on input set 0 (for recall)
+
+
+def make_legs(S, wl, sets, dev, which):
+    """Legs of one workload over the input sets (one set, or four rotating key
+    caches for decode so that the key reads come from HBM, not the 256 MB
+    Infinity Cache)."""
+    import torch
+    inp = sets[0]
+    H, d, B, K = wl.heads, wl.dim, wl.batch, wl.topk
+    fl = 2 * H * d
+    dtype = {"fp8": "fp8", "f32": "f32"}.get(wl.q_fmt, "bf16")
+    decode = wl.n_q < wl.n_k
+    kb = {"fp8": 1, "bf16": 2, "f32": 4}
+    key_bytes = B * wl.n_k * (d * kb[wl.k_fmt] + (4 if wl.k_fmt == "fp8" else 0))
+    dense_pairs = B * causal_pairs(wl.n_q, wl.q_pos0)
+    a = lambda x: dict(q_scale=x["q_scale"], k_scale=x["k_scale"], q_pos0=wl.q_pos0)
+    p0 = S.make_problem(inp["q"], inp["k"], inp["w"], **a(inp))
+    legs = []
+    it = [0]
+
+    def rot():
+        i = it[0] % len(sets)
+        it[0] += 1
+        return i
+
+    if "dense" in which:
+        ws = torch.empty(S.workspace_bytes(p0, S.IDX_OP_SCORE_TOPK, topk=K), dtype=torch.uint8, device=dev)
+        outs = [torch.empty((B, wl.n_q, K), dtype=torch.int32, device=dev) for _ in sets]
+        leg = Leg("dense", None, dense_pairs, B * wl.n_q, "score", "hbm" if decode else "mfma", dtype,
+                  flops=dense_pairs * fl,
+                  hbm_bytes=key_bytes + B * wl.n_q * (H * d * kb[wl.q_fmt] + 4 * H + (4 if wl.q_fmt == "fp8" else 0)))
+
+        def step_dense(leg=leg, ws=ws, outs=outs):
+            i = rot()
+            x = sets[i]
+            S.score_topk(x["q"], x["k"], x["w"], K, workspace=ws, out=outs[i], **a(x))
+            leg.out = outs[0]
+        leg.step = step_dense
+        legs.append(leg)
+
+    for variant in ("refine", "reuse"):
+        if variant not in which or not wl.group:
+            continue
+        G = wl.group
+        C = wl.n_cand if variant == "refine" else K
+        lim = group_limits(wl, G)
+        n_g = len(lim)
+        proxy_pairs = B * sum(x + 1 for x in lim)
+        refine_pairs = B * sum(min(G, wl.n_q - g * G) * min(C, lim[g] + 1) for g in range(n_g)) \
+            if variant == "refine" else 0
+        ws_p = torch.empty(S.workspace_bytes(p0, S.IDX_OP_GROUP_PROXY_SCAN, G, C), dtype=torch.uint8, device=dev)
+        ws_r = torch.empty(max(S.workspace_bytes(p0, S.IDX_OP_REFINE_TOPK, G, C, K), 1), dtype=torch.uint8,
+                           device=dev)
+        cands = [torch.empty((B, n_g, C), dtype=torch.int32, device=dev) for _ in sets]
+        outs = [torch.empty((B, wl.n_q, K), dtype=torch.int32, device=dev) for _ in sets]
+        # the dominant kernel: the re-score for prefill Refine, the proxy scan
+        # otherwise (Reuse's broadcast is cheap; a decode group's proxy scan
+        # streams the whole key cache)
+        if decode:
+            kernel, bound, kdt, fl_k = "proxy_scan", "hbm", "bf16", proxy_pairs * fl
+        elif variant == "refine":
+            kernel, bound, kdt, fl_k = "gather_scan", "mfma", dtype, refine_pairs * fl
+        else:
+            kernel, bound, kdt, fl_k = "proxy_scan", "mfma", "bf16", proxy_pairs * fl
+        leg = Leg(variant, None, proxy_pairs + refine_pairs, B * wl.n_q, kernel, bound, kdt, flops=fl_k,
+                  hbm_bytes=key_bytes + B * n_g * (H * d * 2 + 4 * H))
+
+        def step_grouped(leg=leg, G=G, C=C, variant=variant, ws_p=ws_p, ws_r=ws_r, cands=cands, outs=outs):
+            i = rot()
+            x = sets[i]
+            S.group_proxy_scan(x["q"], x["k"], x["w"], G, C, workspace=ws_p, out=cands[i], **a(x))
+            if variant == "refine":
+                S.refine_topk(x["q"], x["k"], x["w"], cands[i], G, K, workspace=ws_r, out=outs[i], **a(x))
+            else:
+                S.reuse_topk(cands[i], G, wl.n_q, wl.n_k, q_pos0=wl.q_pos0, out=outs[i])
+            leg.out = outs[0]
+        leg.step = step_grouped
+        legs.append(leg)
+    return legs
+
+
+def time_leg(S, leg, steps, warmup):
+    """Wall-clock ms per step over `steps` timed steps (after `warmup`), then
+    the library's per-kernel HIP-event times over as many more steps."""
+    import torch
+    for _ in range(warmup):
+        leg.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        leg.step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    S.profile_read()
+    S.profile_enable(True)
+    t2 = time.perf_counter()
+    for _ in range(steps):
+        leg.step()
+    torch.cuda.synchronize()
+    ms_ev = (time.perf_counter() - t2) / steps * 1e3
+    S.profile_enable(False)
+    prof = S.profile_read()
+    kern = {k: (v[0] / steps, v[1] / steps) for k, v in prof.items() if v[1]}
+    return ms, ms_ev, kern
+
+
+def roofline(leg, kern, workload):
+    """The leg's dominant kernel against its own peak.  Its algorithmic work
+    per step (FLOPs, or HBM bytes for a scan that streams the keys) over its
+    summed launch time per step (a long scan runs as several equal chunks)."""
+    kms, launches = kern.get(leg.kernel, (0.0, 0.0))
+    if kms <= 0:
+        return None
+    r = {"bound": leg.bound, "kernel": leg.kernel, "launches_per_step": launches, "ms_per_step": kms,
+         "launch_ms": kms / max(launches, 1e-9)}
+    if leg.bound == "mfma":
+        ach = leg.flops / (kms * 1e-3) / 1e12
+        r.update(achieved=ach, peak=PEAK_TFLOPS[leg.dtype], unit="TFLOP/s", frac=ach / PEAK_TFLOPS[leg.dtype],
+                 dtype=leg.dtype, flops_per_step=leg.flops)
+    else:
+        ach = leg.hbm_bytes / (kms * 1e-3) / 1e9
+        r.update(achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS, bytes_per_step=leg.hbm_bytes)
+    r["traffic"] = measured_traffic(workload, leg.name)
+    return r
+
+
+def recall_all(approx, exact, chunk=16384):
+    """Recall of every query's dense top-k (sort + batched binary search on the GPU)."""
+    import torch
+    from sparse_attention_token_causal_amd.calibrate import recall
+    a = approx.reshape(-1, approx.shape[-1])
+    e = exact.reshape(-1, exact.shape[-1])
+    rs = torch.cat([recall(a[i:i + chunk], e[i:i + chunk]) for i in range(0, a.shape[0], chunk)])
+    return {"mean": float(rs.mean()), "min": float(rs.min()), "queries": int(rs.numel()),
+            "p01": float(torch.quantile(rs.float(), 0.01))}
+
+
+# ----------------------------------------------------------------------------
+# the CPU oracle on a bounded sample (test infrastructure; timed here only)
+
+
+def oracle_keys(O, synth, inp, b):
+    ks = None if inp["k_scale"] is None else inp["k_scale"][b].cpu().numpy()
+    return O.real_values(synth.raw_numpy(inp["k"][b]), synth.fmt_of(inp["k"]), ks)
+
+
+def oracle_queries(O, synth, inp, b, t0, t1):
+    import numpy as np
+    qs = None if inp["q_scale"] is None else inp["q_scale"][b, t0:t1].cpu().numpy()
+    q = O.real_values(synth.raw_numpy(inp["q"][b, t0:t1]), synth.fmt_of(inp["q"]), qs)
+    return q, inp["w"][b, t0:t1].cpu().numpy().astype(np.float64)
+
+
+def cpu_baseline(wl, inp, variant, seconds):
+    """The oracle as it stands, timed on evenly spaced queries (dense) or whole
+    groups (Refine, Reuse) of the same inputs, until about `seconds` of CPU
+    work or the whole workload; key decoding is outside the timed region."""
+    import numpy as np
+    import oracle as O
+    from sparse_attention_token_causal_amd import synth
+
+    pairs = units = 0
     el = 0.0
     seqs = 0
+    total_units = 0
     for b in range(wl.batch):
-        ks = None if inp["k_scale"] is None else inp["k_scale"][b].cpu().numpy()
-        k = O.real_values(synth.raw_numpy(inp["k"][b]), synth.fmt_of(inp["k"]), ks)
+        k = oracle_keys(O, synth, inp, b)
         seqs += 1
+        if variant == "dense":
+            order = spread_order(wl.n_q)
+            total_units += wl.n_q
+        else:
+            G = wl.group
+            C = wl.n_cand if variant == "refine" else wl.topk
+            lim = group_limits(wl, G)
+            order = spread_order(len(lim))
+            total_units += len(lim)
         t0 = time.perf_counter()
-        for t in order:
-            qs = None if inp["q_scale"] is None else inp["q_scale"][b, t:t + 1].cpu().numpy()
-            q = O.real_values(synth.raw_numpy(inp["q"][b, t:t + 1]), synth.fmt_of(inp["q"]), qs)
-            w = inp["w"][b, t:t + 1].cpu().numpy().astype(np.float64)
-            lim = np.array([wl.q_pos0 + t])
-            I = O.causal_scores(q, k, w, lim)
-            O.select_topk(I[0, : lim[0] + 1], np.arange(lim[0] + 1), wl.topk)
-            pairs += int(lim[0]) + 1
-            done += 1
+        for u in order:
+            if variant == "dense":
+                q, w = oracle_queries(O, synth, inp, b, u, u + 1)
+                p = wl.q_pos0 + u
+                I = O.causal_scores(q, k, w, np.array([p]))
+                O.select_topk(I[0, : p + 1], np.arange(p + 1), wl.topk)
+                pairs += p + 1
+            else:
+                g0, g1 = u * G, min((u + 1) * G, wl.n_q)
+                q, w = oracle_queries(O, synth, inp, b, g0, g1)
+                qb, wb = O.round_proxy(*O.proxy_means(q, w, G), wl.q_fmt)
+                P = O.proxy_scores(qb, wb, k, np.array([lim[u]]))
+                cand = O.proxy_candidates(P, np.array([lim[u]]), C)
+                pairs += lim[u] + 1
+                if variant == "refine":
+                    O.refine_topk(q, k, w, cand, G, wl.q_pos0 + g0, wl.topk)
+                    pairs += (g1 - g0) * min(C, lim[u] + 1)
+                else:
+                    O.reuse_topk(cand, G, wl.q_pos0 + g0, g1 - g0, wl.topk)
+            units += 1
             if el + time.perf_counter() - t0 > seconds:
                 break
         el += time.perf_counter() - t0
         if el > seconds:
             break
-    whole = seqs == wl.batch and done == wl.batch * n
-    what = "every query of every sequence" if whole else f"{done} evenly spaced queries of {seqs} sequence(s)"
-    return {"value": pairs / el, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{what} ({pairs} causal pairs, float64 NumPy, {el:.1f} s, key decoding "
-                      f"excluded); queries/s {done / el:.3g}"}
+    unit, one = ("queries", "query") if variant == "dense" else ("groups", "group")
+    whole = units == total_units
+    what = (f"every {one} of every sequence" if whole else
+            f"{units} evenly spaced {unit} (the last first) of {seqs} sequence(s)")
+    threads = blas_threads()
+    return {"value": pairs / el, "unit": "pairs/s", "cores": int(threads or len(os.sched_getaffinity(0))),
+            "kind": "oracle", "host_cores": len(os.sched_getaffinity(0)), "blas_threads": threads,
+            "sample": f"{what}, {variant} path ({pairs} pairs scored, float64 NumPy, {el:.1f} s)"}
+
+
+# ----------------------------------------------------------------------------
+
+
+def run_workload(S, wl, which, steps, warmup, cpu_secs, headline_leg, dev):
+    """Times the legs of one workload; returns {leg: record}.  cpu_secs: the
+    CPU oracle's time budget per leg (0: none)."""
+    import torch
+    from sparse_attention_token_causal_amd.synth import make_inputs
+
+    decode = wl.n_q < wl.n_k
+    log(f"[bench] {wl.name}: generating inputs")
+    sets = [make_inputs(wl, dev)]
+    if decode:
+        sets += [make_inputs(wl.scaled(seed=wl.seed + i), dev) for i in range(1, 4)]
+    torch.cuda.synchronize()
+    legs = make_legs(S, wl, sets, dev, which)
+    rec = {}
+    dense = None
+    for leg in legs:
+        if leg.name == headline_leg:
+            k_steps, k_warm = steps, warmup
+        elif decode:  # about 75 us per step: enough steps to spread the first launch's latency
+            k_steps, k_warm = max(steps, 200), max(warmup, 5)
+        elif wl.n_q >= 131072 and leg.name == "dense":
+            k_steps, k_warm = min(steps, 10), min(warmup, 2)
+        else:
+            k_steps, k_warm = steps, warmup
+        log(f"[bench] {wl.name} {leg.name}: warmup {k_warm}, timing {k_steps} steps")
+        ms, ms_ev, kern = time_leg(S, leg, k_steps, k_warm)
+        r = {"ms_per_step": ms, "steps": k_steps, "warmup": k_warm, "pairs_per_step": leg.pairs,
+             "pairs_per_s": leg.pairs / (ms * 1e-3), "queries_per_s": leg.queries / (ms * 1e-3),
+             "kernels_ms_per_step": {k: v[0] for k, v in kern.items()},
+             "ms_per_step_with_kernel_events": ms_ev, "roofline": roofline(leg, kern, wl.name)}
+        if leg.name == "dense":
+            dense = (leg, r)
+        elif dense is not None:
+            # every query's dense top-k on the same inputs (input set 0: each
+            # leg's output for it is from the last step that used it)
+            dleg, dr = dense
+            r["dense_equivalent_pairs_per_s"] = dleg.pairs / (ms * 1e-3)
+            r["speedup_vs_dense"] = dr["ms_per_step"] / ms
+            r["recall_vs_dense"] = recall_all(leg.out, dleg.out)
+        rf = r["roofline"]
+        log(f"[bench]   {ms:.3f} ms/step, {r['pairs_per_s']:.3g} pairs/s"
+            + (f", {rf['kernel']} {100 * rf['frac']:.1f}% of the {rf['bound']} peak" if rf else "")
+            + (f", speedup {r['speedup_vs_dense']:.2f}x, recall {r['recall_vs_dense']['mean']:.4f}"
+               if "recall_vs_dense" in r else ""))
+        rec[leg.name] = r
+    for leg in legs:
+        secs = cpu_secs.get(leg.name, 0.0)
+        if secs > 0:
+            log(f"[bench] {wl.name} {leg.name}: timing the CPU oracle for ~{secs:.0f} s")
+            rec[leg.name]["cpu_baseline"] = cpu_baseline(wl, sets[0], leg.name, secs)
+    del legs, sets
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: 200 for a decode workload, 20 otherwise)")
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--steps", type=int, default=20, help="timed steps of the headline leg")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all", help="'all' or one workload name (for profiling runs)")
+    ap.add_argument("--legs", default="dense,refine,reuse", help="legs to run (subset of dense,refine,reuse)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time for the headline leg")
+    ap.add_argument("--cpu-leg-seconds", type=float, default=3.0, help="CPU oracle time for every other leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB (4 times): the known-size reference "
@@ -218,99 +430,58 @@ def main():
                           "bytes_written_per_copy": 4 * n, "copies": 4}))
         return
     import sparse_attention_token_causal_amd as S
-    from sparse_attention_token_causal_amd.synth import WORKLOADS, make_inputs
+    from sparse_attention_token_causal_amd.synth import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    log(f"[bench] workload {wl.name}: generating inputs")
-    inp = make_inputs(wl, dev)
-    torch.cuda.synchronize()
-    step, pairs, flops, queries, dtype, kind = make_step(S, wl, inp, dev)
-    # enough steps that the first launch's latency is spread thin: a decode
-    # step is about 75 us of device time
-    steps = args.steps if args.steps is not None else (200 if kind == "decode" else 20)
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timed region: the steps alone.  The per-kernel durations come from a
-    # second run of the same steps with the library's HIP events around each
-    # launch (on the launch stream); the events add a few microseconds per
-    # launch, which matters for the short decode step, so they stay out of
-    # the step time.
-    log(f"[bench] timing {steps} steps")
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    s_per_step = (t1 - t0) / steps
-    S.profile_read()  # drop anything recorded before
-    S.profile_enable(True)
-    torch.cuda.synchronize()
-    log(f"[bench] timing the kernels of {steps} more steps (HIP events per launch)")
-    t2 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    t3 = time.perf_counter()
-    S.profile_enable(False)
-    prof = S.profile_read()
-    score_ms, score_n = prof["score"]
-    sel_ms, sel_n = prof["select"]
-    per_launch_ms = score_ms / max(score_n, 1)
-    launches_per_step = score_n / steps
-    flops_per_launch = flops / max(launches_per_step, 1e-9)
-    achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[dtype]
-    traffic = measured_traffic(wl.name)
-    roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": traffic,
-            "kernel": "score (Q.K^T on MFMA + fused ReLU/weight/head-sum epilogue)",
-            "launch_ms": per_launch_ms, "flops_per_launch": flops_per_launch}
-    if kind == "decode":
-        # the decode scan streams the key cache: algorithmic bytes per launch =
-        # keys (+ per-token scales) + queries + head weights, each read once
-        kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_fmt]
-        qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_fmt]
-        key_bytes = wl.batch * wl.n_k * (wl.dim * kb + (4 if wl.k_fmt == "fp8" else 0))
-        q_bytes = wl.batch * wl.n_q * (wl.heads * wl.dim * qb + wl.heads * 4 + (4 if wl.q_fmt == "fp8" else 0))
-        alg = (key_bytes + q_bytes) / max(launches_per_step, 1e-9)
-        gbs = alg / (per_launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
-                "kernel": "split-key scan (streams the key cache; MFMA + fused epilogue)",
-                "launch_ms": per_launch_ms, "bytes_per_launch": alg, "flops_per_launch": flops_per_launch}
-    result = {
+    names = ORDER if args.workload == "all" else [args.workload]
+    head = HEADLINE if args.workload == "all" else args.workload
+    which = set(args.legs.split(","))
+    results = {}
+    head_leg = None
+    for name in names:
+        wl = WORKLOADS[name]
+        wl_which = which if wl.group else {"dense"} & which
+        leg0 = "refine" if (wl.group and wl.n_q == wl.n_k and "refine" in wl_which) else sorted(wl_which)[0]
+        if name == head:
+            head_leg = leg0
+        cpu = {} if args.no_cpu_baseline else {
+            leg: (args.cpu_seconds if (name == head and leg == head_leg) else args.cpu_leg_seconds)
+            for leg in wl_which}
+        results[name] = run_workload(S, wl, wl_which, args.steps, args.warmup, cpu,
+                                     head_leg if name == head else None, dev)
+
+    wl = WORKLOADS[head]
+    h = results[head][head_leg]
+    dtype = {"fp8": "fp8", "f32": "f32"}.get(wl.q_fmt, "bf16")
+    out = {
         "metric": METRIC,
-        "value": pairs / s_per_step,
+        "value": h["pairs_per_s"],
         "unit": "pairs/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": args.warmup,
-        "ms_per_step": s_per_step * 1e3,
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k,
-                   "heads": wl.heads, "dim": wl.dim, "topk": wl.topk, "q_storage": wl.q_fmt,
+        "config": {"workload": wl.name, "path": {"refine": "PIVOT-Refine", "reuse": "PIVOT-Reuse",
+                                                 "dense": "dense scan"}[head_leg],
+                   "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k, "heads": wl.heads, "dim": wl.dim,
+                   "topk": wl.topk, "group": wl.group, "n_cand": wl.n_cand, "q_storage": wl.q_fmt,
                    "k_storage": wl.k_fmt, "parallelism": "single GPU"},
-        "queries_per_s": queries / s_per_step,
-        "pairs_per_step": pairs,
-        "kernels_ms_per_step": {k: v[0] / steps for k, v in prof.items() if v[1]},
-        "ms_per_step_with_kernel_events": (t3 - t2) / steps * 1e3,
-        "roofline": roof,
-        "cpu_baseline": None,
+        "queries_per_s": h["queries_per_s"],
+        "roofline": h["roofline"],
+        "cpu_baseline": h.get("cpu_baseline"),
+        "legs": results[head],
+        "workloads": {n: r for n, r in results.items() if n != head},
     }
-    log(f"[bench] {result['ms_per_step']:.3f} ms/step, score {per_launch_ms:.3f} ms/launch "
-        f"({roof['achieved']:.1f} {roof['unit']}, {100 * roof['frac']:.1f}% of the {roof['bound']} peak), select "
-        f"{sel_ms / max(sel_n, 1):.3f} ms/launch")
-    if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    for k in ("dense_equivalent_pairs_per_s", "speedup_vs_dense", "recall_vs_dense"):
+        if k in h:
+            out[k] = h[k]
+    log(f"[bench] headline {wl.name} {head_leg}: {h['ms_per_step']:.3f} ms/step, {h['pairs_per_s']:.4g} pairs/s")
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -287,14 +287,17 @@ int32_t idx_ivf_route(const idx_problem* p, int32_t group, int32_t n_clusters, i
  * on the same stream; idx_profile_read synchronizes on the recorded events
  * and reports, per kernel kind, the summed duration in milliseconds and the
  * number of launches since the last read (then clears the records).
- * Kinds: 0 score (MFMA scan), 1 select (top-k), 2 proxy build, 3 reuse,
- * 4 fill (debug score dumps, counter clears), 5 IVF index build (the whole
- * build), 6 IVF routing (cluster scores and list expansion), 7 rescan of
- * the dense scan's overflowed candidate lists.  Returns IDX_EHIP on an event
- * error.  Not reentrant: enable it from one host thread only. */
+ * Kinds: 0 dense score scan (the MFMA scan of idx_score_topk, tiled or
+ * split-key), 1 select (top-k), 2 proxy build (and block means), 3 reuse
+ * (and block expansion), 4 fill (debug score dumps, counter clears), 5 IVF
+ * index build (the whole build), 6 IVF routing (cluster scores and list
+ * expansion), 7 rescan of the dense scan's overflowed candidate lists,
+ * 8 proxy scan (group proxies or block means against the keys), 9 gather
+ * scan (PIVOT-Refine re-score of the candidates).  Returns IDX_EHIP on an
+ * event error.  Not reentrant: enable it from one host thread only. */
 enum { IDX_KERNEL_SCORE = 0, IDX_KERNEL_SELECT = 1, IDX_KERNEL_PROXY = 2, IDX_KERNEL_REUSE = 3,
        IDX_KERNEL_FILL = 4, IDX_KERNEL_IVF_BUILD = 5, IDX_KERNEL_IVF_ROUTE = 6, IDX_KERNEL_RESCAN = 7,
-       IDX_KERNEL_KINDS = 8 };
+       IDX_KERNEL_PROXY_SCAN = 8, IDX_KERNEL_GATHER_SCAN = 9, IDX_KERNEL_KINDS = 10 };
 int32_t idx_profile_enable(int32_t on);
 int32_t idx_profile_read(float* ms /* [IDX_KERNEL_KINDS] */, int32_t* launches /* [IDX_KERNEL_KINDS] */);
 

@@ -212,18 +212,19 @@ def score_topk_static(q, k, w, topk, q_scale=None, k_scale=None, q_pos0=None, ou
 
 
 def group_proxy_scan(q, k, w, group, n_cand, q_scale=None, k_scale=None, q_pos0=None,
-                     return_proxy=False, return_scores=False, workspace=None):
+                     return_proxy=False, return_scores=False, workspace=None, out=None):
     """PIVOT proxy + shared scan: candidates int32 [B, n_g, n_cand] (-1 padded).
 
     ``return_proxy`` adds the stored proxy (q as bfloat16, or float32 for
     float32 q; w float32); ``return_scores`` adds the proxy scores [B, n_g, n_k].
+    ``out`` may supply the candidate tensor.
     """
+    B, n_q, H, d = q.shape
+    n_g = -(-n_q // group)
+    cand = _check_out(out, (B, n_g, n_cand), q)
     _check_workspace_tensor(workspace, q)
     lib = load_library()
     p = make_problem(q, k, w, q_scale, k_scale, q_pos0)
-    B, n_q, H, d = q.shape
-    n_g = -(-n_q // group)
-    cand = torch.empty((B, n_g, n_cand), dtype=torch.int32, device=q.device)
     pq = pw = ps = None
     if return_proxy:
         pq = torch.empty((B, n_g, H, d), dtype=torch.float32 if q.dtype == torch.float32 else torch.bfloat16,
@@ -396,7 +397,8 @@ def ivf_route(q, k, w, index, group, insert_batch, n_cand, q_scale=None, k_scale
     return res[0] if len(res) == 1 else tuple(res)
 
 
-KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill", "ivf_build", "ivf_route", "rescan")
+KERNEL_KINDS = ("score", "select", "proxy", "reuse", "fill", "ivf_build", "ivf_route", "rescan", "proxy_scan",
+                "gather_scan")
 
 
 def profile_enable(on=True):

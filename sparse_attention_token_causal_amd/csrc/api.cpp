@@ -51,7 +51,7 @@ hipError_t timed(int kind, hipStream_t st, F launch) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr size_t kScoreBufferTarget = size_t(1) << 30;  // score rows buffered per chunk (bytes)
+constexpr size_t kScoreBufferTarget = size_t(2) << 30;  // score rows buffered per chunk (bytes)
 // Candidate lists of a filtering dense scan buffered per chunk (bytes): the
 // workspace of idx_score_topk stays below this (plus a few bytes per row
 // block) at any sequence length.
@@ -194,13 +194,15 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     const long long r0 = block_start_row(L.mode, blk0, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
     const long long r1 = block_start_row(L.mode, blk0 + nb, L.total_blocks, B, L.n_rows, n_q, group, L.BQ);
     if (r1 <= r0) continue;
-    // Split the key columns when there are few row blocks: aim for about two
-    // workgroups per CU with at least 16 key tiles each (long scans such as
-    // decode), and for at least one per CU on short scans.  Filtering keeps
-    // whole rows in one workgroup.
+    // Split the key columns when there are few row blocks: aim for about
+    // eight workgroups per CU with at least 16 key tiles each (the causal
+    // limit leaves the chunks beyond a row block's last key empty, so the
+    // busy ones number far fewer: the proxy scans of long sequences, whose
+    // 2048 proxies make 256 row blocks), and for at least one per CU on short
+    // scans.  Filtering keeps whole rows in one workgroup.
     int chunks = 1;
-    if (nb < 512 && !flt.on) {
-      chunks = std::max(1, std::min(ceil_div(512, nb), ceil_div(L.n_cols, 16 * tw)));
+    if (nb < 2048 && !flt.on) {
+      chunks = std::max(1, std::min(ceil_div(2048, nb), ceil_div(L.n_cols, 16 * tw)));
       if ((long long)nb * chunks < 256) chunks = std::min(ceil_div(256, nb), ceil_div(L.n_cols, tw));
     }
     int kc = ceil_div(L.n_cols, chunks);
@@ -229,7 +231,9 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.topk = topk;
     sa.ovf_count = flt.on ? flt.ovf_cnt + blk0 / bpc : nullptr;
     sa.ovf_list = flt.ovf_list;
-    if (timed(IDX_KERNEL_SCORE, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
+    const int kind = L.mode == kModeGather ? IDX_KERNEL_GATHER_SCAN
+                     : (L.mode == kModeDense ? IDX_KERNEL_SCORE : IDX_KERNEL_PROXY_SCAN);
+    if (timed(kind, st, [&] { return launch_score(sa, qf, kf, H, D, chunks, st); }) != hipSuccess)
       return IDX_EHIP;
     if (flt.on) {
       // rows whose candidates overflowed their list: a fixed grid of
@@ -446,7 +450,7 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   a.win = (uint32_t*)(region + sl.win);
   a.wbase = (int*)(region + sl.wbase);
   a.n_chunks = sl.chunks;
-  if (timed(IDX_KERNEL_SCORE, st, [&] {
+  if (timed(mode == kModeDense ? IDX_KERNEL_SCORE : IDX_KERNEL_PROXY_SCAN, st, [&] {
         return launch_split_scan(a, qf, p->k_dtype, p->heads, p->dim, B, sl.chunks, st);
       }) != hipSuccess)
     return IDX_EHIP;

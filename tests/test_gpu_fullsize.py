@@ -4,9 +4,12 @@ Every output row is checked for the invariants that hold at any size (distinct
 causal indices, -1 padding at the end, the expected count); sampled rows and
 groups are checked against the oracle, which computes them one by one:
 scores within tolerance, the select bit-exact on the GPU's own scores, and
-banded set agreement with the oracle's own top-k.  Grouped runs also check
-the proxy, the candidate select and Reuse exactly, and report recall against
-the dense top-k (a measurement, not a parity bar).
+banded set agreement with the oracle's own top-k.  The grouped workloads also
+run the dense scan at their full size (262144 and 131072 tokens) in the timed
+configuration, check the proxy, the candidate select and Reuse exactly, check
+that Refine equals dense wherever a group's whole prefix fits the candidate
+budget, and report recall of the GPU dense top-k over every query (a
+measurement, not a parity bar).
 """
 
 import gc
@@ -17,6 +20,7 @@ import torch
 
 import oracle as O
 import sparse_attention_token_causal_amd as S
+from sparse_attention_token_causal_amd.calibrate import recall
 from sparse_attention_token_causal_amd.synth import WORKLOADS, make_inputs
 
 from parity import (AGREEMENT, ATOL, RTOL, assert_same_sets, band_agreement, check_rows_valid, check_scores,
@@ -137,12 +141,54 @@ def test_decode_fp8k_B8_n131072():
     print(f"  decode-group Refine recall vs dense: {np.mean(recalls):.4f}", flush=True)
 
 
-def grouped_fullsize(wl, sample_groups, dense_queries):
+def dense_fullsize(wl, inp, starts, m=32):
+    """The dense scan at full size as timed (the library's own workspace:
+    bounded candidate lists, several chunks): the invariants on every row;
+    for each sampled run of m consecutive queries, the score-dump path on a
+    sub-problem (those queries against the keys up to the last of them: the
+    same kernel arithmetic), whose scores are checked against the oracle
+    (D1), whose select is bit-exact on its own scores (D2), whose sets equal
+    the timed path's, and band agreement with the oracle's top-k (D3)."""
+    a = args(inp, wl)
+    idx = S.score_topk(inp["q"], inp["k"], inp["w"], wl.topk, **a)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    all_rows_valid(idx_np, wl)
+    k_full = real_rows(inp, 0, [0])[1]
+    for t0 in starts:
+        assert t0 % 8 == 0 and wl.q_pos0 == 0
+        sl = slice(t0, t0 + m)
+        sub = lambda x, s2: None if x is None else x[:, s2].contiguous()
+        idx_d, sc = S.score_topk(sub(inp["q"], sl), sub(inp["k"], slice(0, t0 + m)), sub(inp["w"], sl), wl.topk,
+                                 q_scale=sub(inp["q_scale"], sl), k_scale=sub(inp["k_scale"], slice(0, t0 + m)),
+                                 q_pos0=t0, return_scores=True)
+        torch.cuda.synchronize()
+        idx_d, sc = idx_d[0].cpu().numpy(), sc[0].cpu().numpy()
+        rows = list(range(t0, t0 + m))
+        q, _, w = real_rows(inp, 0, rows)
+        lim = np.asarray(rows)
+        I = O.causal_scores(q, k_full[: t0 + m], w, lim)
+        check_scores(sc, I, f"{wl.name} dense scores t0={t0}")
+        own = [O.select_topk(sc[i, : lim[i] + 1].astype(np.float64), np.arange(lim[i] + 1), wl.topk) for i in range(m)]
+        assert_same_sets(idx_d, own, f"{wl.name} select on own scores t0={t0}")
+        assert_same_sets(idx_np[0, sl], idx_d, f"{wl.name} timed path vs dump path t0={t0}")
+        ora = [O.select_topk(I[i, : lim[i] + 1], np.arange(lim[i] + 1), wl.topk) for i in range(m)]
+        ora = np.array([np.pad(r, (0, wl.topk - len(r)), constant_values=-1) for r in ora])
+        agr = band_agreement(idx_np[0, sl], ora, I)
+        assert agr >= AGREEMENT, f"{wl.name}: dense set agreement {agr} at t0={t0}"
+    print(f"  dense at full size: every row valid, {len(starts)} x {m} sampled rows match the dump path "
+          f"and the oracle", flush=True)
+    return idx
+
+
+def grouped_fullsize(wl, sample_groups, dense_queries, dense_starts):
     dev = cuda()
     print(f"\n[full] {wl.name}", flush=True)
     inp = make_inputs(wl, dev)
     free()
     a = args(inp, wl)
+    dense_gpu = dense_fullsize(wl, inp, dense_starts)
+    free()
     G, C, K = wl.group, wl.n_cand, wl.topk
     n_g = -(-wl.n_q // G)
     lim = O.proxy_limits(wl.n_q, G, wl.q_pos0)
@@ -164,6 +210,19 @@ def grouped_fullsize(wl, sample_groups, dense_queries):
     ptop = S.group_proxy_scan(inp["q"], inp["k"], inp["w"], G, K, **a)
     uidx = S.reuse_topk(ptop, G, wl.n_q, wl.n_k, q_pos0=wl.q_pos0)
     torch.cuda.synchronize()
+    # recall of the GPU dense top-k over every query (a measurement), and an
+    # exact identity: where a group's whole prefix fits the candidate budget
+    # its candidates are that prefix, so Refine (the same scores) is dense
+    rec_r = recall(ridx, dense_gpu)
+    rec_u = recall(uidx, dense_gpu)
+    full_prefix = (torch.as_tensor(lim, device=dev) + 1 <= C).repeat_interleave(G)[: wl.n_q]
+    n_exact = int(full_prefix.sum())
+    srt = lambda x: torch.sort(x[0][full_prefix], dim=-1)[0]
+    assert n_exact > 0 and torch.equal(srt(ridx), srt(dense_gpu)), "Refine over a whole prefix is not dense"
+    print(f"  all {wl.n_q} queries vs the GPU dense top-k: Refine recall mean {float(rec_r.mean()):.4f} "
+          f"min {float(rec_r.min()):.4f}; Reuse recall mean {float(rec_u.mean()):.4f} min {float(rec_u.min()):.4f}; "
+          f"{n_exact} queries with the whole prefix as candidates: Refine = dense", flush=True)
+    del dense_gpu
     cand_np, ptop_np = cand.cpu().numpy()[0], ptop.cpu().numpy()[0]
     ridx_np, uidx_np = ridx.cpu().numpy(), uidx.cpu().numpy()
     pq_s = pq[0].index_select(0, g_t).float().cpu().numpy().astype(np.float64)
@@ -234,11 +293,13 @@ def test_grouped_refine_bf16_L131072():
     wl = WORKLOADS["grouped_refine_bf16_L131072_G64_C8192_k2048"]
     n_g = wl.n_q // wl.group
     grouped_fullsize(wl, [0, 100, n_g // 2, n_g - 1],
-                     [int(x) for x in np.linspace(wl.n_q // 8, wl.n_q - 1, 12)])
+                     [int(x) for x in np.linspace(wl.n_q // 8, wl.n_q - 1, 12)],
+                     [4096, wl.n_q // 2, wl.n_q - 32])
 
 
 def test_grouped_fp8_L262144():
     wl = WORKLOADS["grouped_fp8_L262144_G128_C8192_k2048"]
     n_g = wl.n_q // wl.group
     grouped_fullsize(wl, [0, 50, n_g // 2, n_g - 1],
-                     [int(x) for x in np.linspace(wl.n_q // 8, wl.n_q - 1, 8)])
+                     [int(x) for x in np.linspace(wl.n_q // 8, wl.n_q - 1, 8)],
+                     [8192, wl.n_q // 2, wl.n_q - 32])
