@@ -8,8 +8,9 @@ shared proxy scan to 8192 candidates, each member's own re-score and top-2048),
 one step = proxy build + proxy scan + candidate select + gathered re-score +
 per-query select ("PIVOT: Efficient Query-Group Indexing for Token-Level
 Sparse Attention", Abstract).  The same workload's dense scan (the full-scan
-baseline on the same inputs) and PIVOT-Reuse are timed beside it as legs, and
-the other four workloads (the 1024-token float32 and 32K-token bfloat16 dense
+baseline on the same inputs), PIVOT-Reuse, and PIVOT-Refine at the cheapest
+(group size, budget) of a sweep that reached a recall of 0.99 are timed
+beside it as legs, and the other four workloads (the 1024-token float32 and 32K-token bfloat16 dense
 prefills, the 8 x 2 decode step over 131072 FP8 keys with its decode grouping,
 and PIVOT-Refine at 131072 bfloat16 tokens) follow as sub-records.
 
@@ -42,6 +43,13 @@ HEADLINE = "grouped_fp8_L262144_G128_C8192_k2048"
 ORDER = ["prefill_f32_L1024_H16_d64_k128", "prefill_bf16_L32768_H64_d128_k2048",
          "decode_fp8k_B8_mtp2_n131072_H64_d128_k2048", "grouped_refine_bf16_L131072_G64_C8192_k2048",
          HEADLINE]
+
+# PIVOT-Refine at the cheapest (group size, candidate budget) of a sweep on
+# these inputs whose recall of the dense top-k, averaged over every query,
+# reached 0.99 (262K fp8: G 32, C 16384 gave 0.996 where G 64, C 16384 gave
+# 0.9897; 131K bf16: G 16, C 16384 gave 0.994 where G 32, C 16384 gave 0.984)
+RECALL99 = {"grouped_fp8_L262144_G128_C8192_k2048": (32, 16384),
+            "grouped_refine_bf16_L131072_G64_C8192_k2048": (16, 16384)}
 
 # MI355X published dense peaks (no sparsity), TFLOP/s, and HBM3E GB/s.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
@@ -165,16 +173,15 @@ def make_legs(S, wl, sets, dev, which):
         leg.step = step_dense
         legs.append(leg)
 
-    for variant in ("refine", "reuse"):
-        if variant not in which or not wl.group:
+    for variant in ("refine", "reuse", "refine_r99"):
+        if variant not in which or not wl.group or (variant == "refine_r99" and wl.name not in RECALL99):
             continue
-        G = wl.group
-        C = wl.n_cand if variant == "refine" else K
+        G, C = RECALL99[wl.name] if variant == "refine_r99" else (wl.group, wl.n_cand if variant == "refine" else K)
         lim = group_limits(wl, G)
         n_g = len(lim)
         proxy_pairs = B * sum(x + 1 for x in lim)
         refine_pairs = B * sum(min(G, wl.n_q - g * G) * min(C, lim[g] + 1) for g in range(n_g)) \
-            if variant == "refine" else 0
+            if variant != "reuse" else 0
         ws_p = torch.empty(S.workspace_bytes(p0, S.IDX_OP_GROUP_PROXY_SCAN, G, C), dtype=torch.uint8, device=dev)
         ws_r = torch.empty(max(S.workspace_bytes(p0, S.IDX_OP_REFINE_TOPK, G, C, K), 1), dtype=torch.uint8,
                            device=dev)
@@ -185,18 +192,19 @@ def make_legs(S, wl, sets, dev, which):
         # streams the whole key cache)
         if decode:
             kernel, bound, kdt, fl_k = "proxy_scan", "hbm", "bf16", proxy_pairs * fl
-        elif variant == "refine":
+        elif variant != "reuse":
             kernel, bound, kdt, fl_k = "gather_scan", "mfma", dtype, refine_pairs * fl
         else:
             kernel, bound, kdt, fl_k = "proxy_scan", "mfma", "bf16", proxy_pairs * fl
         leg = Leg(variant, None, proxy_pairs + refine_pairs, B * wl.n_q, kernel, bound, kdt, flops=fl_k,
                   hbm_bytes=key_bytes + B * n_g * (H * d * 2 + 4 * H))
+        leg.group, leg.n_cand = G, C
 
         def step_grouped(leg=leg, G=G, C=C, variant=variant, ws_p=ws_p, ws_r=ws_r, cands=cands, outs=outs):
             i = rot()
             x = sets[i]
             S.group_proxy_scan(x["q"], x["k"], x["w"], G, C, workspace=ws_p, out=cands[i], **a(x))
-            if variant == "refine":
+            if variant != "reuse":
                 S.refine_topk(x["q"], x["k"], x["w"], cands[i], G, K, workspace=ws_r, out=outs[i], **a(x))
             else:
                 S.reuse_topk(cands[i], G, wl.n_q, wl.n_k, q_pos0=wl.q_pos0, out=outs[i])
@@ -278,7 +286,7 @@ def oracle_queries(O, synth, inp, b, t0, t1):
     return q, inp["w"][b, t0:t1].cpu().numpy().astype(np.float64)
 
 
-def cpu_baseline(wl, inp, variant, seconds):
+def cpu_baseline(wl, inp, variant, seconds, G=None, C=None):
     """The oracle as it stands, timed on evenly spaced queries (dense) or whole
     groups (Refine, Reuse) of the same inputs, until about `seconds` of CPU
     work or the whole workload; key decoding is outside the timed region."""
@@ -297,8 +305,8 @@ def cpu_baseline(wl, inp, variant, seconds):
             order = spread_order(wl.n_q)
             total_units += wl.n_q
         else:
-            G = wl.group
-            C = wl.n_cand if variant == "refine" else wl.topk
+            G = G or wl.group
+            C = C or (wl.n_cand if variant == "refine" else wl.topk)
             lim = group_limits(wl, G)
             order = spread_order(len(lim))
             total_units += len(lim)
@@ -317,7 +325,7 @@ def cpu_baseline(wl, inp, variant, seconds):
                 P = O.proxy_scores(qb, wb, k, np.array([lim[u]]))
                 cand = O.proxy_candidates(P, np.array([lim[u]]), C)
                 pairs += lim[u] + 1
-                if variant == "refine":
+                if variant != "reuse":
                     O.refine_topk(q, k, w, cand, G, wl.q_pos0 + g0, wl.topk)
                     pairs += (g1 - g0) * min(C, lim[u] + 1)
                 else:
@@ -361,13 +369,14 @@ def run_workload(S, wl, which, steps, warmup, cpu_secs, headline_leg, dev):
             k_steps, k_warm = steps, warmup
         elif decode:  # about 75 us per step: enough steps to spread the first launch's latency
             k_steps, k_warm = max(steps, 200), max(warmup, 5)
-        elif wl.n_q >= 131072 and leg.name == "dense":
+        elif wl.n_q >= 131072 and leg.name in ("dense", "refine_r99"):
             k_steps, k_warm = min(steps, 10), min(warmup, 2)
         else:
             k_steps, k_warm = steps, warmup
         log(f"[bench] {wl.name} {leg.name}: warmup {k_warm}, timing {k_steps} steps")
         ms, ms_ev, kern = time_leg(S, leg, k_steps, k_warm)
         r = {"ms_per_step": ms, "steps": k_steps, "warmup": k_warm, "pairs_per_step": leg.pairs,
+             **({"group": leg.group, "n_cand": leg.n_cand} if hasattr(leg, "group") else {}),
              "pairs_per_s": leg.pairs / (ms * 1e-3), "queries_per_s": leg.queries / (ms * 1e-3),
              "kernels_ms_per_step": {k: v[0] for k, v in kern.items()},
              "ms_per_step_with_kernel_events": ms_ev, "roofline": roofline(leg, kern, wl.name)}
@@ -390,7 +399,8 @@ def run_workload(S, wl, which, steps, warmup, cpu_secs, headline_leg, dev):
         secs = cpu_secs.get(leg.name, 0.0)
         if secs > 0:
             log(f"[bench] {wl.name} {leg.name}: timing the CPU oracle for ~{secs:.0f} s")
-            rec[leg.name]["cpu_baseline"] = cpu_baseline(wl, sets[0], leg.name, secs)
+            rec[leg.name]["cpu_baseline"] = cpu_baseline(wl, sets[0], leg.name, secs, getattr(leg, "group", None),
+                                                         getattr(leg, "n_cand", None))
     del legs, sets
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -403,7 +413,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20, help="timed steps of the headline leg")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all", help="'all' or one workload name (for profiling runs)")
-    ap.add_argument("--legs", default="dense,refine,reuse", help="legs to run (subset of dense,refine,reuse)")
+    ap.add_argument("--legs", default="dense,refine,reuse,refine_r99",
+                    help="legs to run (subset of dense,refine,reuse,refine_r99)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle time for the headline leg")
     ap.add_argument("--cpu-leg-seconds", type=float, default=3.0, help="CPU oracle time for every other leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -467,9 +478,11 @@ def main():
         "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "path": {"refine": "PIVOT-Refine", "reuse": "PIVOT-Reuse",
+                                                 "refine_r99": "PIVOT-Refine at the recall-0.99 setting",
                                                  "dense": "dense scan"}[head_leg],
                    "batch": wl.batch, "n_q": wl.n_q, "n_k": wl.n_k, "heads": wl.heads, "dim": wl.dim,
-                   "topk": wl.topk, "group": wl.group, "n_cand": wl.n_cand, "q_storage": wl.q_fmt,
+                   "topk": wl.topk, "group": h.get("group", wl.group), "n_cand": h.get("n_cand", wl.n_cand),
+                   "q_storage": wl.q_fmt,
                    "k_storage": wl.k_fmt, "parallelism": "single GPU"},
         "queries_per_s": h["queries_per_s"],
         "roofline": h["roofline"],
