@@ -270,34 +270,54 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // Loads are unconditional: a column past the range or an empty candidate
   // slot reads a valid key row (it is masked in the epilogue), so the loads
   // of a tile are all in flight together while the current tile computes.
+  // The FP8 key scales travel with the key rows (loaded with them, two tiles
+  // ahead): a scale loaded only when the tile is stored would expose a full
+  // memory latency before every tile's barrier.
   i32x4 stage_buf[2][NCH];
   int stage_keys[2][NCH];
+  float stage_scl[2][NCH];
+  // Gathered columns: the key indices of a tile are read from LDS one tile
+  // before its loads are issued (stage_index), so that the loads do not wait
+  // for an LDS round trip.
+  auto stage_index = [&](auto set_c, int c0) {
+    if constexpr (GATHER) {
+      constexpr int SET = decltype(set_c)::value;
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        const int i = min((int)threadIdx.x + u * kScoreThreads, TW * CPC - 1);
+        const int j = i / CPC;
+        int s = s_cand[min(c0 + j, c_end - 1) - c_begin];
+        if (c0 + j >= c_end || s >= a.n_k) s = -1;
+        stage_keys[SET][u] = s;
+      }
+    }
+  };
   auto stage_load = [&](auto set_c, int c0) {
     constexpr int SET = decltype(set_c)::value;
     i32x4* stage = stage_buf[SET];
     int* stage_key = stage_keys[SET];
+    float* stage_sc = stage_scl[SET];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
       const int i = min((int)threadIdx.x + u * kScoreThreads, TW * CPC - 1);
       const int j = i / CPC, c = i % CPC;
-      const int col = min(c0 + j, c_end - 1);
-      int s, srow;
+      int srow;
       if (GATHER) {
-        s = s_cand[col - c_begin];
-        if (c0 + j >= c_end || s >= a.n_k) s = -1;
-        srow = s < 0 ? 0 : s;
+        srow = max(stage_key[u], 0);
       } else {
-        s = c0 + j < c_end ? col : -1;
+        const int col = min(c0 + j, c_end - 1);
+        stage_key[u] = c0 + j < c_end ? col : -1;
         srow = col;
       }
-      stage_key[u] = s;
       stage[u] = *(const i32x4*)(kseq + ((size_t)srow * D * M::GE) + c * 16);
+      if constexpr (KF == FP8) stage_sc[u] = a.k_scale[(size_t)b * a.n_k + srow];
     }
   };
   auto stage_store = [&](auto set_c, int buf) {
     constexpr int SET = decltype(set_c)::value;
     const i32x4* stage = stage_buf[SET];
     const int* stage_key = stage_keys[SET];
+    const float* stage_sc = stage_scl[SET];
     char* kt = smem + buf * TILE_BYTES;
     int* ck = (int*)(kt + TW * ROWB);
     float* cs = (float*)(ck + TW);
@@ -320,14 +340,16 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
         if (COLINFO && c == 0) {
           const int s = stage_key[u];
           ck[j] = s;
-          cs[j] = (s >= 0 && KF == FP8) ? a.k_scale[(size_t)b * a.n_k + s] : 1.f;
+          cs[j] = (s >= 0 && KF == FP8) ? stage_sc[u] : 1.f;
         }
       }
     }
   };
 
   // ---- MFMA of one 32-column block over d, from LDS buffer `buf` ----
-  f32x16 acc[2][2];
+  // (zero before the first tile: its epilogue reads the blocks of a tile
+  // that does not exist, and discards them)
+  f32x16 acc[2][2] = {};
   // With few inner steps (bf16, fp8) the fragments of a block are read from
   // LDS ahead of its MFMAs: block 0's at the top of the tile, block 1's while
   // block 0 computes.  Float32 (64 steps) reads step by step.
@@ -508,9 +530,12 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // set P holds the tiles of parity P between their load and their store).
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  stage_index(S0{}, c_begin);
   stage_load(S0{}, c_begin);
+  stage_index(S1{}, c_begin + TW);
   if (c_begin + TW < c_end) stage_load(S1{}, c_begin + TW);
   stage_store(S0{}, 0);
+  stage_index(S0{}, c_begin + 2 * TW);
   __syncthreads();
   int buf = 0, prev_c0 = c_begin, key_prev = -1;
   float scale_prev = 1.f;
@@ -534,6 +559,9 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       scale_cur = ((const float*)(ck + TW))[jl];
     }
     if constexpr (PRELOAD) load_block(bfA, buf, 0);
+    // the previous tile's block 0 partials while block 0's fragments arrive
+    // (they are consumed before block 0's MFMAs overwrite its accumulators)
+    partial(0, p0_prev);
     // block 0 MFMAs || the previous tile's block 1 partials and its epilogue
     // (nothing is stored on the first tile) || block 1 fragment reads
     mfma_block(bfA, buf, 0);
@@ -541,24 +569,29 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, c0 != c_begin);
     if constexpr (PRELOAD) load_block(bfB, buf, 1);
     IDX_INTERLEAVE(0, true);
-    // block 1 MFMAs || block 0 partials
+    // block 1 MFMAs (their partials run at the top of the next tile)
     mfma_block(bfB, buf, 1);
-    partial(0, p0_prev);
-    IDX_INTERLEAVE(1, false);
     if constexpr (FILTER == 1) {
       if ((((c0 - c_begin) / TW) & 7) == 7) advance_theta();
     }
     if (c0 + TW < c_end) stage_store(Nxt{}, buf ^ 1);
+    stage_index(Nxt{}, c0 + 3 * TW);
     __syncthreads();
     prev_c0 = c0;
     key_prev = key_cur;
     scale_prev = scale_cur;
     buf ^= 1;
   };
-  for (int c0 = c_begin; c0 < c_end; c0 += 2 * TW) {
+  // whole pairs of tiles, then an odd last tile (a loop body without a
+  // conditional second tile: the compiler's wait counts at the loop head
+  // then only see the path where both staging sets were consumed)
+  int c0 = c_begin;
+  for (; c0 + TW < c_end; c0 += 2 * TW) {
     tile(S0{}, c0);
-    if (c0 + TW < c_end) tile(S1{}, c0 + TW);
+    tile(S1{}, c0 + TW);
   }
+  if (c0 < c_end) tile(S0{}, c0);
+  partial(0, p0_prev);
   partial(1, p1);
   epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, true);
   // The bin where the count from the top of `hist` reaches `need`: returns
