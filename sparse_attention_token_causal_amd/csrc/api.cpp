@@ -491,8 +491,12 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   se.gidx = (int*)(region + sl.gidx);
   se.topk = topk;
   se.out = out;
-  // lists hold the rows' top-k plus the rest of the threshold bin
-  const int expect = (int)std::min<long long>(p->n_k, 8LL * topk);
+  // lists hold the rows' top-k plus the rest of the threshold bin (on the
+  // decode workload 2.3-4.8 k entries for k 2048 and 8.3-14.6 k for the
+  // proxies' k 8192); the hint picks the variant that keeps up to 16384 of
+  // them in registers unless k itself calls for more (a longer list streams)
+  const int expect =
+      (int)std::min<long long>(p->n_k, std::max(2LL * topk, std::min(8LL * topk, 16384LL)));
   if (timed(IDX_KERNEL_SELECT, st, [&] {
         hipError_t e = launch_split_compact(c, R, st);
         return e != hipSuccess ? e : launch_select_list(se, R, expect, st);

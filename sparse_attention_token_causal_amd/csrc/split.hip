@@ -405,21 +405,29 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   __syncthreads();
   const int* wb = a.wbase + (size_t)row * a.n_chunks;
   const uint32_t* wn = a.win + (size_t)row * a.n_chunks * kSplitWin;
-  // batches of 8 windows' entries per thread: all loads in flight together
+  // runs of four window entries per thread (16-byte loads; a run never
+  // crosses a window), eight runs per thread per batch: all loads in flight
+  // together (one batch for up to 64 chunks)
   const int n_e = a.n_chunks * kSplitWin;
-  for (int e0 = 0; e0 < n_e; e0 += 8 * 256) {
-    uint32_t cv[8];
+  static_assert(kSplitWin % 4 == 0, "runs of four entries");
+  for (int e0 = 0; e0 < n_e; e0 += 8 * 4 * 256) {
+    uint4 cv[8];
     int bv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = min(e0 + u * 256 + tid, n_e - 1);
+      const int e = min(e0 + 4 * (u * 256 + tid), n_e - 4);
       bv[u] = wb[e / kSplitWin];
-      cv[u] = wn[e];
+      cv[u] = *(const uint4*)(wn + e);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * 256 + tid;
-      if (e < n_e && bv[u] >= 0 && cv[u]) atomicAdd(&hist[bv[u] + e % kSplitWin], cv[u]);
+      const int e = e0 + 4 * (u * 256 + tid);
+      if (e < n_e && bv[u] >= 0) {
+        const uint32_t c4[4] = {cv[u].x, cv[u].y, cv[u].z, cv[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (c4[q]) atomicAdd(&hist[bv[u] + e % kSplitWin + q], c4[q]);
+      }
     }
   }
   __syncthreads();
