@@ -172,9 +172,12 @@ struct Filter {
   int* ovf_list = nullptr;  // [blocks per chunk] overflowed row blocks of the current chunk
 };
 
+// grec (gathered columns only, may be null): [buf_rows, kFiltInfoStride]
+// records of each row's exact boundary bin, written by the scan when one
+// workgroup sees a row's every column, for the select's one-pass path.
 int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D, int B, int n_q,
                      int group, float* buf, long long buf_rows, bool full, int topk, int* out,
-                     hipStream_t st, const Filter& flt = Filter()) {
+                     hipStream_t st, const Filter& flt = Filter(), int* grec = nullptr) {
   const int bpc_max = full ? L.total_blocks : (int)(buf_rows / L.BQ);
   if (bpc_max < 1) return IDX_EWORKSPACE;
   // chunks of equal size (a short last chunk would run a launch of a few
@@ -215,6 +218,8 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
       kc = std::min(kc, std::min(kCandLdsMax, fit));
     }
     chunks = ceil_div(L.n_cols, kc);
+    const bool recs = grec && L.mode == kModeGather && chunks == 1 && H == 64 && L.rw == 8 &&
+                      score_lds_bytes(qf, kf, D, L.rw, L.nw, 3, kc) <= kScoreLdsMax;
     sa.blk0 = blk0;
     sa.n_blocks = nb;
     sa.row0 = full ? 0 : r0;
@@ -223,10 +228,10 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     sa.kc = kc;
     sa.rw = L.rw;
     sa.nw = L.nw;
-    sa.filter = flt.on ? 1 : 0;
+    sa.filter = flt.on ? 1 : (recs ? 3 : 0);
     sa.cval = flt.val;
     sa.cidx = flt.idx;
-    sa.ccount = flt.count;
+    sa.ccount = recs ? grec : flt.count;
     sa.cld = flt.on ? flt.cap : L.n_cols;
     sa.topk = topk;
     sa.ovf_count = flt.on ? flt.ovf_cnt + blk0 / bpc : nullptr;
@@ -258,6 +263,7 @@ int score_and_select(ScoreArgs sa, const Layout& L, int qf, int kf, int H, int D
     se.cand = sa.cand;
     se.lidx = nullptr;
     se.counts = nullptr;
+    se.finfo = recs ? grec : nullptr;
     se.topk = topk;
     se.out = out;
     if (flt.on) {
@@ -667,7 +673,8 @@ size_t idx_workspace_bytes(const idx_problem* p, int32_t op, int32_t group, int3
   if (op == IDX_OP_REFINE_TOPK) {
     if (n_cand < 1) return 0;
     Layout L = make_layout(kModeGather, p, p->n_q, n_cand, group);
-    return align_up((size_t)buffer_rows(L, (long long)p->batch * p->n_q) * n_cand * 4);
+    const long long rows = buffer_rows(L, (long long)p->batch * p->n_q);
+    return align_up((size_t)rows * n_cand * 4) + align_up((size_t)rows * kFiltInfoStride * 4);
   }
   return 0;
 }
@@ -797,6 +804,7 @@ int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand
   Layout L = make_layout(kModeGather, p, p->n_q, n_cand, group);
   const bool full = out_cand_scores != nullptr;
   float* buf;
+  int* recs = nullptr;  // the rows' boundary records (workspace path only)
   long long rows;
   if (full) {
     buf = out_cand_scores;
@@ -804,8 +812,9 @@ int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand
   } else {
     const size_t need = idx_workspace_bytes(p, IDX_OP_REFINE_TOPK, group, n_cand, topk);
     if (!ws || ws_bytes < need) return IDX_EWORKSPACE;
+    rows = buffer_rows(L, (long long)p->batch * p->n_q);
     buf = (float*)ws;
-    rows = (long long)(ws_bytes / ((size_t)n_cand * 4));
+    recs = (int*)((char*)ws + align_up((size_t)rows * n_cand * 4));
   }
   ScoreArgs sa = base_args(p);
   sa.group = group;
@@ -813,7 +822,7 @@ int32_t idx_refine_topk(const idx_problem* p, int32_t group, const int32_t* cand
   sa.cand = cand;
   sa.mode = kModeGather;
   return score_and_select(sa, L, p->q_dtype, p->k_dtype, p->heads, p->dim, p->batch, p->n_q,
-                          group, buf, rows, full, topk, out_idx, st);
+                          group, buf, rows, full, topk, out_idx, st, Filter(), recs);
 }
 
 int32_t idx_reuse_topk(const idx_problem* p, int32_t group, const int32_t* proxy_topk,

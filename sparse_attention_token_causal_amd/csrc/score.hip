@@ -107,7 +107,9 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 // score, a window of 8 octaves placed from the first tile's largest score).
 
 // FILTER: 0 full score rows; 1 the filtering scan (candidate lists); 2 the
-// rescan of the row blocks whose lists overflowed (see ScoreArgs::filter).
+// rescan of the row blocks whose lists overflowed; 3 full score rows of
+// gathered columns plus each row's record of its exact boundary bin (see
+// ScoreArgs::filter).
 template <int QF, int KF, int H, int D, int RW, bool GATHER, int NWV, int FILTER>
 __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   constexpr int kScoreThreads = NWV * 64;  // threads of this workgroup
@@ -124,7 +126,8 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // per-column data (key index, key scale) is only needed for gathered
   // columns or FP8 keys; dense scans of BF16/F32 keys use the position itself
   constexpr bool COLINFO = GATHER || KF == FP8;
-  static_assert(FILTER == 0 || (!GATHER && QW == 1), "filtering: dense scans, one query per wave");
+  static_assert(FILTER == 0 || (QW == 1 && (GATHER ? FILTER == 3 : FILTER != 3)),
+                "filtering: dense scans, records: gathered columns; one query per wave");
 
   // two tile buffers: [TW][ROWB] key rows, then TW column keys and TW scales
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -243,7 +246,8 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // The scan counts every candidate (f_cnt) and stores the first cld of
   // them; the rescan counts the interval's keys in `hist` (bins of
   // 2^r_shift above r_lo) and, on a tied interval, c_cnt of its keys so far.
-  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES) + wave * kFiltBins;
+  // (after the candidate indices when the columns are gathered)
+  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES + (GATHER ? (a.kc * 4 + 15) / 16 * 16 : 0)) + wave * kFiltBins;
   int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0, c_cnt = 0;
   float f_lo = neg_inf();  // lower edge of bin f_theta (-inf while f_theta == 0)
   bool f_based = false;
@@ -251,8 +255,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   int* f_idx = nullptr;
   if constexpr (FILTER != 0) {
     for (int i = l; i < kFiltBins; i += kWave) hist[i] = 0;
-    f_val = a.cval + crow * a.cld;
-    f_idx = a.cidx + crow * a.cld;
+    if constexpr (FILTER != 3) {
+      f_val = a.cval + crow * a.cld;
+      f_idx = a.cidx + crow * a.cld;
+    }
   }
 
   // Gathered columns: the workgroup's candidate key indices are copied to
@@ -432,8 +438,22 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       const bool mine = live && t < r_end && col < c_end;
       const bool ok = mine && key >= 0 && key <= qlim[qi];
       const float val = ok ? (KF == FP8 ? tot * scale : tot) : neg_inf();
-      if constexpr (FILTER == 0) {
+      if constexpr (FILTER == 0 || FILTER == 3) {
         if (mine) a.out[((size_t)b * a.n_rows + t - a.row0) * a.ld + col] = val;
+        if constexpr (FILTER == 3) {
+          // every eligible score in the row's histogram (bins placed from the
+          // first tile as in the filtering scan)
+          if (!f_based) {
+            uint32_t m = ok ? order_key(val) : 0u;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+            if (m != 0u) {
+              f_base = (int)(m >> 15) - (kFiltBins - 512);
+              f_based = true;
+            }
+          }
+          if (ok) atomicAdd(&hist[min(max((int)(order_key(val) >> 15) - f_base, 0), kFiltBins - 1)], 1u);
+        }
       } else if constexpr (FILTER == 2) {
         // Rescan: keys above the interval are always stored; the interval's
         // keys are stored while they fit and counted in the class histogram,
@@ -615,6 +635,23 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     }
     return -2;
   };
+  if constexpr (FILTER == 3) {
+    // The row's exact boundary bin and the count above it, when this
+    // workgroup saw every column of the row; the select then writes the bins
+    // above it and ranks only that bin (the general path otherwise: a large
+    // or clamped boundary bin, fewer eligible keys than topk, or columns
+    // split over workgroups).
+    int above, cnt_b;
+    const int bstar = boundary_bin(a.topk, above, cnt_b);
+    if (l == 0 && t_first < r_end) {
+      const bool whole = a.kc >= a.n_cols;
+      info[kFiltInfoCount] = a.n_cols;
+      info[kFiltInfoBase] = f_base;
+      info[kFiltInfoBoundary] =
+          (whole && bstar > 0 && bstar < kFiltBins - 1 && cnt_b <= kFiltBoundaryMax) ? bstar : -1;
+      info[kFiltInfoAbove] = above;
+    }
+  }
   if constexpr (FILTER == 1) {
     // The histogram counts every candidate in its bin, so the bin where the
     // count from the top reaches topk (and the count above it) is exact:
@@ -705,7 +742,9 @@ static hipError_t launch_one(const ScoreArgs& a, dim3 grid, size_t lds, hipStrea
   if constexpr (H == 64 && RW == 8) {
     if (a.filter == 1 && !g) return launch_mode<QF, KF, H, D, 8, false, 8, 1>(a, grid, lds, st);
     if (a.filter == 2 && !g) return launch_mode<QF, KF, H, D, 8, false, 8, 2>(a, grid, lds, st);
+    if (a.filter == 3 && g) return launch_mode<QF, KF, H, D, 8, true, 8, 3>(a, grid, lds, st);
   }
+  if (a.filter != 0) return hipErrorInvalidValue;
   if (RW == 4 && a.nw == 4)
     return g ? launch_mode<QF, KF, H, D, 4, true, 4>(a, grid, lds, st)
              : launch_mode<QF, KF, H, D, 4, false, 4>(a, grid, lds, st);
@@ -740,10 +779,10 @@ size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int ga
   const int ke = (qf == F32) ? 4 : (qf == BF16 ? 2 : 1);
   const int tw = (nw / rw) * 64;
   (void)kf;
-  // double-buffered tiles, then one filtering histogram and one flag per
-  // wave (dense scans) or the workgroup's candidate key indices (gather)
-  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) +
-         (filter ? (size_t)nw * (kFiltBins * 4 + 4) : 0) + (size_t)gather_cols * 4;
+  // double-buffered tiles, the workgroup's candidate key indices (gather),
+  // then one filtering histogram and one flag per wave
+  return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) + ((size_t)gather_cols * 4 + 15) / 16 * 16 +
+         (filter ? (size_t)nw * (kFiltBins * 4 + 4) : 0);
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,

@@ -128,11 +128,13 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
   }
   if (a.mode == kModeList) crow = a.lidx + (long long)blockIdx.x * a.ld;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  if (FLIST && a.mode == kModeList && a.finfo) {
-    // A filtered list with its scan's record: one pass writes every
-    // candidate above the boundary bin (there are exactly `above` of them),
-    // collects the boundary bin's candidates (at most kFiltBoundaryMax), and
-    // those are ranked exactly by (score descending, key ascending).
+  if (FLIST && (a.mode == kModeList || a.mode == kModeGather) && a.finfo) {
+    // A filtered list (or a gathered row) with its scan's record: one pass
+    // writes every candidate above the boundary bin (there are exactly
+    // `above` of them), collects the boundary bin's candidates (at most
+    // kFiltBoundaryMax), and those are ranked exactly by (score descending,
+    // key ascending).  Excluded entries (-inf, gathered rows only) are in
+    // no bin.
     const int* fi = a.finfo + kFiltInfoStride * (long long)blockIdx.x;
     const int bstar = fi[kFiltInfoBoundary];
     if (bstar != -1) {
@@ -149,12 +151,12 @@ __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArg
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int c = min(c0 + j * NT + tid, n - 1);
-          k[j] = order_key(row[c]);
+          k[j] = load_key(row, c);
           x[j] = crow[c];
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const bool in = c0 + j * NT + tid < n;
+          const bool in = c0 + j * NT + tid < n && k[j] != kKeyExcluded;
           const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
           wn[j] = in && (all || bin > bstar);
           bnd[j] = in && !all && bin == bstar;
@@ -578,6 +580,11 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
   // with 512 threads; a longer list streams inside the kernel
   if (a.mode == kModeList) return a.finfo ? launch_kpt<256, 32, false, true>(a, n_launch_rows, st)
                                           : launch_kpt<256, 32>(a, n_launch_rows, st);
+  // gathered rows with their scan's records: the one-pass variant (its
+  // general path keeps 8192 keys in registers; 16384 for longer rows)
+  if (a.mode == kModeGather && a.finfo)
+    return a.n_cols <= 256 * 32 ? launch_kpt<256, 32, false, true>(a, n_launch_rows, st)
+                                : launch_kpt<1024, 16, false, true>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
   const int classes[4] = {256 * 8, 256 * 32, 1024 * 16, 1024 * 32};
   long long r = 0;
