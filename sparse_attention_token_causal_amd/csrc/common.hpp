@@ -77,6 +77,19 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+// Wave-wide maximum of an unsigned int on DPP lane moves (the same row
+// shifts and broadcasts as the prefix sum, with max for +), returned
+// wave-uniform.  Every lane must be active.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
 // Wave-wide sum (every lane active), returned wave-uniform.
 __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);

@@ -444,9 +444,9 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
           // every eligible score in the row's histogram (bins placed from the
           // first tile as in the filtering scan)
           if (!f_based) {
-            uint32_t m = ok ? order_key(val) : 0u;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+            // (DPP lane moves: a chain of LDS-routed shuffles here was
+            // executed on every tile, its latency exposed each time)
+            const uint32_t m = wave_max_u32(ok ? order_key(val) : 0u);
             if (m != 0u) {
               f_base = (int)(m >> 15) - (kFiltBins - 512);
               f_based = true;
@@ -488,9 +488,9 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
         // Only passing scores are counted: bins under the threshold are never
         // consulted again.
         if (!f_based) {
-          uint32_t m = ok ? order_key(val) : 0u;
-#pragma unroll
-          for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+          // (DPP lane moves: a chain of LDS-routed shuffles here was
+          // executed on every tile, its latency exposed each time)
+          const uint32_t m = wave_max_u32(ok ? order_key(val) : 0u);
           if (m != 0u) {
             f_base = (int)(m >> 15) - (kFiltBins - 512);
             f_based = true;
