@@ -386,6 +386,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     }
   };
   constexpr int NDSR = NKS * (int)(sizeof(frag_t) / 16);  // 16-byte LDS reads per block
+  // Where a tile's block 0 partial sums run: beside block 1's MFMAs when
+  // those take longer than the sums (bf16: 16 MFMAs of 32 cycles per block;
+  // float32), else at the top of the next tile (FP8: 4 MFMAs of 64 cycles).
+  constexpr bool LATE0 = M::KSTEP <= 16;
   // one MFMA per few VALU ops, optionally with the next block's fragment reads spread in
 #define IDX_INTERLEAVE(id, reads)                                                      \
   if constexpr (PRELOAD) {                                                             \
@@ -579,9 +583,9 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
       scale_cur = ((const float*)(ck + TW))[jl];
     }
     if constexpr (PRELOAD) load_block(bfA, buf, 0);
-    // the previous tile's block 0 partials while block 0's fragments arrive
-    // (they are consumed before block 0's MFMAs overwrite its accumulators)
-    partial(0, p0_prev);
+    // FP8: the previous tile's block 0 partials while block 0's fragments
+    // arrive (consumed before block 0's MFMAs overwrite its accumulators)
+    if constexpr (!LATE0) partial(0, p0_prev);
     // block 0 MFMAs || the previous tile's block 1 partials and its epilogue
     // (nothing is stored on the first tile) || block 1 fragment reads
     mfma_block(bfA, buf, 0);
@@ -589,8 +593,16 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, c0 != c_begin);
     if constexpr (PRELOAD) load_block(bfB, buf, 1);
     IDX_INTERLEAVE(0, true);
-    // block 1 MFMAs (their partials run at the top of the next tile)
+    // block 1 MFMAs || (bf16, float32) this tile's block 0 partials, kept
+    // here by an empty use (the compiler would sink them past the barrier
+    // into the next tile's serial start)
     mfma_block(bfB, buf, 1);
+    if constexpr (LATE0) {
+      partial(0, p0_prev);
+#pragma unroll
+      for (int qi = 0; qi < QW; ++qi) __asm__ __volatile__("" ::"v"(p0_prev[qi]));
+      IDX_INTERLEAVE(1, false);
+    }
     if constexpr (FILTER == 1) {
       if ((((c0 - c_begin) / TW) & 7) == 7) advance_theta();
     }
@@ -611,7 +623,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     tile(S1{}, c0 + TW);
   }
   if (c0 < c_end) tile(S0{}, c0);
-  partial(0, p0_prev);
+  if constexpr (!LATE0) partial(0, p0_prev);
   partial(1, p1);
   epilogue(p0_prev, p1, prev_c0, key_prev, scale_prev, true);
   // The bin where the count from the top of `hist` reaches `need`: returns
