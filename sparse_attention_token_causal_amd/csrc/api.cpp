@@ -400,13 +400,13 @@ int split_seg(const idx_problem* p, int n_rows) {
 
 struct SplitLayout {
   int kc, chunks, seg, segs;
-  size_t scores, win, wbase, cval, cidx, segcnt, gval, gidx, total;  // byte offsets
+  size_t scores, win, wbase, cval, cidx, segcnt, gval, gidx, thr, total;  // byte offsets
 };
 
 // Region, R = B * n_rows: [R, n_k] scores | [R, chunks, kSplitWin] windows |
 // [R, chunks] window bases | [R, n_k] candidate scores | [R, n_k] candidate
 // keys | [R, segs] segment counts | [R, n_k] gathered scores | [R, n_k]
-// gathered keys.
+// gathered keys | [R] threshold bins.
 SplitLayout split_layout(const idx_problem* p, int n_rows) {
   const size_t R = (size_t)p->batch * n_rows, row = (size_t)p->n_k * 4;
   SplitLayout s;
@@ -423,6 +423,7 @@ SplitLayout split_layout(const idx_problem* p, int n_rows) {
   s.segcnt = o;  o += align_up(R * s.segs * 4);
   s.gval = o;    o += align_up(R * row);
   s.gidx = o;    o += align_up(R * row);
+  s.thr = o;     o += align_up(R * 4);
   s.total = o;
   return s;
 }
@@ -478,13 +479,14 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   c.cval = (float*)(region + sl.cval);
   c.cidx = (int*)(region + sl.cidx);
   c.segcnt = (int*)(region + sl.segcnt);
+  c.thr = (int*)(region + sl.thr);
   SelectArgs se = {};
   se.scores = c.cval;
   se.ld = p->n_k;
   se.row0 = 0;
   se.n_rows = n_rows;
   se.n_cols = p->n_k;
-  se.mode = kModeList;
+  se.mode = mode;
   se.q_pos0 = p->q_pos0;
   se.n_q = p->n_q;
   se.group = group;
@@ -497,15 +499,9 @@ int split_score_select(const idx_problem* p, int qf, const void* q, const float*
   se.gidx = (int*)(region + sl.gidx);
   se.topk = topk;
   se.out = out;
-  // lists hold the rows' top-k plus the rest of the threshold bin (on the
-  // decode workload 2.3-4.8 k entries for k 2048 and 8.3-14.6 k for the
-  // proxies' k 8192); the hint picks the variant that keeps up to 16384 of
-  // them in registers unless k itself calls for more (a longer list streams)
-  const int expect =
-      (int)std::min<long long>(p->n_k, std::max(2LL * topk, std::min(8LL * topk, 16384LL)));
   if (timed(IDX_KERNEL_SELECT, st, [&] {
         hipError_t e = launch_split_compact(c, R, st);
-        return e != hipSuccess ? e : launch_select_list(se, R, expect, st);
+        return e != hipSuccess ? e : launch_split_select(se, c.thr, R, st);
       }) != hipSuccess)
     return IDX_EHIP;
   return IDX_OK;

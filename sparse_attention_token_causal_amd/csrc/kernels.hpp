@@ -126,6 +126,7 @@ hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_
 hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st);
 // Split-key scan (few rows per sequence, long key axis): see split.hip.
 constexpr int kSplitBins = 4096;   // per-row histogram of the top 12 order-key bits
+constexpr int kSplitShift = 32 - 12;  // histogram bin = order key >> kSplitShift
 constexpr int kSplitWin = 128;     // histogram bins a scan workgroup reports per row
 constexpr int kSplitMaxRows = 4;   // rows (queries or proxies) per sequence
 constexpr int kMaxSegs = 256;      // segments of a segmented list
@@ -195,13 +196,17 @@ struct CompactArgs {
   float* cval;            // [B * n_rows, n_k]: segment s's candidates from s * seg
   int* cidx;              // [B * n_rows, n_k] their key indices
   int* segcnt;            // [B * n_rows, n_segs] candidates per segment
+  int* thr;               // [B * n_rows] each row's threshold bin (order key >> kSplitShift)
 };
 
 hipError_t launch_split_scan(const SplitArgs& a, int qf, int kf, int H, int D, int B, int chunks,
                              hipStream_t st);
 hipError_t launch_split_compact(const CompactArgs& a, int rows, hipStream_t st);
-// List select with a row-length hint (the variant that keeps that many keys in registers).
-hipError_t launch_select_list(const SelectArgs& a, int n_launch_rows, int expect_len, hipStream_t st);
+// Top-k of the split-key scan's rows from the compaction's candidate lists
+// and threshold bins (see select.hip): `a` describes the rows (mode,
+// positions, n_rows, n_cols = n_k, topk, out) and the segmented lists
+// (scores/lidx, seg_counts, n_segs, seg_len, ld = n_k, gval/gidx scratch).
+hipError_t launch_split_select(const SelectArgs& a, const int* thr, int rows, hipStream_t st);
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
 hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* w, int B, int n_q,
                               int H, int D, int qf, int group, void* pq, float* pw,

@@ -42,7 +42,6 @@
 
 namespace idx {
 
-constexpr int kSplitShift = 32 - 12;  // histogram bin = order key >> kSplitShift
 // gfx9 sched_group_barrier instruction classes
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
 
@@ -383,7 +382,10 @@ __global__ __launch_bounds__(256, 2) void split_scan_kernel(SplitArgs a) {
 // A window covers the bins of its chunk from kSplitWin below the chunk's top
 // non-empty bin; counts below a window are dropped, so the summed histogram
 // can only undercount, the threshold bin only comes out lower, and the list
-// can only grow: it always holds the row's top-k.
+// can only grow: it always holds the row's top-k.  The segment's first batch
+// of scores is loaded together with the windows (it does not depend on the
+// threshold); the first segment's workgroup records the row's threshold bin
+// for the select.
 __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   __shared__ uint32_t hist[kSplitBins];
   __shared__ int wtot[4];
@@ -399,6 +401,16 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
     return;
   }
   const int need = min(a.topk, len);
+
+  // the first batch of the segment's scores, in flight with the window loads
+  constexpr int kBatch = 16 * 256;
+  const float* srow = a.scores + (size_t)row * a.n_k;
+  float v[16];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = srow[min(c0 + u * 256 + tid, s1 - 1)];
+  };
+  load_batch(s0);
 
   for (int i = tid; i < kSplitBins; i += 256) hist[i] = 0u;
   if (tid == 0) s_thr = 0;
@@ -433,8 +445,8 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   __syncthreads();
 
   // Block-wide exclusive prefix sum of one int per thread (+ the total).
-  auto block_scan = [&](int v, int* total) {
-    const int incl = wave_incl_scan(v);
+  auto block_scan = [&](int x, int* total) {
+    const int incl = wave_incl_scan(x);
     if (l == kWave - 1) wtot[wave] = incl;
     __syncthreads();
     int before = 0, tot = 0;
@@ -445,7 +457,7 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
     }
     __syncthreads();
     *total = tot;
-    return before + incl - v;
+    return before + incl - x;
   };
 
   // thread i owns bins [16 i, 16 i + 16): the threshold is the highest bin
@@ -473,24 +485,21 @@ __global__ __launch_bounds__(256) void split_compact_kernel(CompactArgs a) {
   __syncthreads();
   const uint32_t thr = (uint32_t)s_thr;
 
-  const float* srow = a.scores + (size_t)row * a.n_k;
+  if (blockIdx.x == 0 && tid == 0) a.thr[row] = (int)thr;
+
   float* cv = a.cval + (size_t)row * a.n_k + s0;
   int* ci = a.cidx + (size_t)row * a.n_k + s0;
   int filled = 0;
-  for (int c0 = s0; c0 < s1; c0 += 16 * 256) {
-    float v[16];
+  for (int c0 = s0; c0 < s1; c0 += kBatch) {
+    if (c0 != s0) load_batch(c0);
     uint32_t pm = 0;
-    int n = 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int col = c0 + u * 256 + tid;
-      v[u] = srow[min(col, s1 - 1)];
-      const bool p = col < s1 && (order_key(v[u]) >> kSplitShift) >= thr;
-      pm |= (uint32_t)p << u;
-      n += p;
+      pm |= (uint32_t)(col < s1 && (order_key(v[u]) >> kSplitShift) >= thr) << u;
     }
     int tot;
-    int o = filled + block_scan(n, &tot);
+    int o = filled + block_scan(__builtin_popcount(pm), &tot);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if ((pm >> u) & 1u) {

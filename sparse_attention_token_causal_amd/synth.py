@@ -51,7 +51,7 @@ class Workload:
     q_fmt: str          # "f32" | "bf16" | "fp8"
     k_fmt: str
     q_dist: str         # "normal8" | "ar1" | "int"
-    k_dist: str         # "normal8" | "heavy" | "int" | "const" | "ramp" | "clustered"
+    k_dist: str         # "normal8" | "heavy" | "int" | "const" | "ramp" | "spikes" | "clustered"
     rho: float = 0.0
     topk: int = 2048
     group: int = 0      # 0: dense only
@@ -145,6 +145,10 @@ def make_inputs(wl: Workload, device="cpu"):
     elif wl.k_dist == "ramp":
         ramp = torch.arange(1, nk + 1, device=device, dtype=torch.float32).reshape(1, nk, 1) / nk
         k = ramp * k[:, :1].abs()
+    elif wl.k_dist == "spikes":
+        # every 16th key 2^20 times larger (exact in every storage format)
+        k = k / 8.0
+        k[:, ::16] *= float(2 ** 20)
     elif wl.k_dist == "heavy":
         n_heavy = nk // 100
         for b in range(B):

@@ -67,14 +67,19 @@ DENSE = [
              seed=17, w_dist="int"),
     Workload("split_fp8_nq4_H16_d64_k2000", 1, 4, 2500, 16, 64, "fp8", "fp8", "normal8", "normal8",
              topk=2000, seed=18),
-    # lists of 8193..16384 expected entries take the list select that loads
-    # segments directly: every segment fits (normal keys), and every score of
-    # a query ties so that every key is a candidate and the segments overflow
-    # into the gathering path (the shorter lists above always gather)
-    Workload("split_segd_nq2_n12000_k1500", 1, 2, 12000, 64, 128, "bf16", "bf16", "normal8", "heavy",
+    # long candidate lists (k 1500 of 12000); then the split select's general
+    # path: every score of a query ties (the threshold bin holds more entries
+    # than the lean path keeps), and keys whose scores spread over more octaves
+    # above the threshold than a chunk's histogram window covers (more than k
+    # entries above the bin)
+    Workload("split_lists_nq2_n12000_k1500", 1, 2, 12000, 64, 128, "bf16", "bf16", "normal8", "heavy",
              topk=1500, seed=19),
     Workload("split_ties_const_keys_nq2_n20000_k1100", 1, 2, 20000, 64, 128, "bf16", "bf16", "normal8", "const",
              topk=1100, seed=20),
+    Workload("split_spikes_nq2_n20000_k2000", 1, 2, 20000, 64, 128, "bf16", "bf16", "normal8", "spikes",
+             topk=2000, seed=21),
+    Workload("split_spikes_fp8_B2_nq1_n9000_k700", 2, 1, 9000, 64, 128, "fp8", "fp8", "ar1", "spikes",
+             rho=0.99, topk=700, seed=22),
 ]
 
 
