@@ -42,6 +42,7 @@ struct SelectShared {
   int wred[3][kMaxNW];
   int wscan[kMaxNW];
   int list_n;
+  int out_n;  // output slots reserved (the streaming variant's last pass)
   uint32_t sel_bin;
   int sel_above;
   // fallback radix state
@@ -331,7 +332,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
   // or its `need` best entries in (key desc, index asc) order.
   uint32_t blo = kmin, bhi = kmax;
   int above = 0, need = kk, in_bin = n_valid;
-  bool idx_radix = false;
+  bool idx_radix = false, gather_late = false;
   int idx_thr = 0;
 
   // Suffix scan over the histogram: picks the bin holding rank `need`
@@ -371,10 +372,26 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         const float x = __builtin_fmaf(key_to_float(k), scale, off);
         return (uint32_t)min(max((int)x, 0), kBins - 1);
       };
-      for (int i = tid; i < kBins; i += kSelectThreads) sh.hist[i] = 0;
+      // (KPT == 0: each bin's key range is kept in the list arrays during
+      // the same pass, so the row is not read again for it)
+      static_assert(kListCap >= kBins, "a key range per bin");
+      for (int i = tid; i < kBins; i += kSelectThreads) {
+        sh.hist[i] = 0;
+        if constexpr (KPT == 0) {
+          sh.lkey[i] = 0xFFFFFFFFu;
+          sh.lidx[i] = 0;
+        }
+      }
       __syncthreads();
       for_keys([&](int, uint32_t k, int) {
-        if (k != kKeyExcluded) atomicAdd(&sh.hist[lbin(k)], 1u);
+        if (k != kKeyExcluded) {
+          const uint32_t bn = lbin(k);
+          atomicAdd(&sh.hist[bn], 1u);
+          if constexpr (KPT == 0) {
+            atomicMin(&sh.lkey[bn], k);
+            atomicMax((uint32_t*)&sh.lidx[bn], k);
+          }
+        }
       });
       __syncthreads();
       int before;
@@ -382,6 +399,11 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
       above += before;
       need -= before;
       in_bin = (int)sh.hist[b];
+      if constexpr (KPT == 0) {
+        blo = sh.lkey[b];
+        bhi = (uint32_t)sh.lidx[b];
+        __syncthreads();
+      } else {
       // the key range of that bin
       uint32_t mn = 0xFFFFFFFFu, mx = 0u;
       for_keys([&](int, uint32_t k, int) {
@@ -408,6 +430,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         bhi = max(bhi, (uint32_t)sh.wred[2][i]);
       }
       __syncthreads();
+      }
     }
     // 2b. MSB-first radix descent in 11-bit digits inside [blo, bhi]
     while (in_bin > kRankMax && blo != bhi && in_bin != need) {
@@ -436,7 +459,9 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
       __syncthreads();
     }
     if (in_bin != need) {
-      if (in_bin <= kListCap) {
+      if (KPT == 0 && in_bin <= kListCap) {
+        gather_late = true;  // in the streaming variant's single last pass
+      } else if (in_bin <= kListCap) {
         // ---- 3. gather the boundary interval and rank it exactly ----
         if (tid == 0) sh.list_n = 0;
         __syncthreads();
@@ -506,6 +531,65 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
   auto certain = [&](uint32_t k) -> bool {
     return k != kKeyExcluded && (k > cut_hi || (whole && k >= cut_lo));
   };
+  if constexpr (KPT == 0) {
+    if (!idx_radix) {
+      // one pass over the row: the winners above the interval go to the
+      // output at slots reserved once per wave and batch (a row is a set),
+      // and the interval's keys, when they are ranked, to the LDS list
+      if (tid == 0) {
+        sh.list_n = 0;
+        sh.out_n = 0;
+      }
+      __syncthreads();
+      for (int c0 = 0; c0 < len; c0 += 8 * kSelectThreads) {
+        float v[8];
+        int x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int cc = min(c0 + j * kSelectThreads + tid, max(len - 1, 0));
+          v[j] = row[cc];
+          x[j] = indexed ? crow[cc] : cc;
+        }
+        uint32_t cm = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + j * kSelectThreads + tid;
+          const uint32_t k = (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded;
+          cm |= (uint32_t)certain(k) << j;
+          if (gather_late && k != kKeyExcluded && k >= cut_lo && k <= cut_hi) {
+            const int slot = atomicAdd(&sh.list_n, 1);
+            sh.lkey[slot] = k;
+            sh.lidx[slot] = x[j];
+          }
+        }
+        const int n = __builtin_popcount(cm);
+        const int incl = wave_incl_scan(n);
+        const int wt = __builtin_amdgcn_readlane(incl, kWave - 1);
+        int base = 0;
+        if (lane == kWave - 1 && wt) base = atomicAdd(&sh.out_n, wt);
+        int pos = __builtin_amdgcn_readlane(base, kWave - 1) + incl - n;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((cm >> j) & 1u) out[pos++] = x[j];
+      }
+      if (gather_late) {
+        __syncthreads();
+        const int m = sh.list_n;
+        for (int i = tid; i < m; i += kSelectThreads) {
+          const uint32_t ki = sh.lkey[i];
+          const int xi = sh.lidx[i];
+          int rank = 0;
+          for (int j = 0; j < m; ++j) {
+            const uint32_t kj = sh.lkey[j];
+            rank += (kj > ki) || (kj == ki && sh.lidx[j] < xi);
+          }
+          if (rank < need) out[above + rank] = xi;
+        }
+      }
+      for (int i = kk + tid; i < topk; i += kSelectThreads) out[i] = -1;
+      return;
+    }
+  }
   int mine = 0;
   for_keys([&](int, uint32_t k, int) { mine += certain(k); });
   int total;

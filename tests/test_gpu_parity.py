@@ -80,6 +80,17 @@ DENSE = [
              topk=2000, seed=21),
     Workload("split_spikes_fp8_B2_nq1_n9000_k700", 2, 1, 9000, 64, 128, "fp8", "fp8", "ar1", "spikes",
              rho=0.99, topk=700, seed=22),
+    # rows longer than 32768 keys take the streaming select (rows re-read
+    # from global memory): a spread row, tie-heavy rows, a row of equal
+    # keys, and k beyond the row
+    Workload("stream_nq8_n40000_H16_k1000", 1, 8, 40000, 16, 64, "bf16", "bf16", "normal8", "heavy",
+             topk=1000, seed=23),
+    Workload("stream_ties_int_nq6_n36000_H16_k3000", 1, 6, 36000, 16, 64, "bf16", "bf16", "int", "int",
+             topk=3000, seed=24, w_dist="int"),
+    Workload("stream_const_keys_nq5_n34000_H32_k700", 1, 5, 34000, 32, 64, "bf16", "bf16", "normal8", "const",
+             topk=700, seed=25),
+    Workload("stream_f32_nq5_n33000_H16_k40000", 1, 5, 33000, 16, 64, "f32", "f32", "normal8", "normal8",
+             topk=40000, seed=26),
 ]
 
 
