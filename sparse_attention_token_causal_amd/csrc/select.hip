@@ -5,15 +5,140 @@
 
 namespace idx {
 
-template <int NT, int KPT, bool FLIST = false>
+template <int NT, int KPT>
 __global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArgs a) {
   __shared__ SelectShared sh;
-  select_row<NT, KPT, FLIST>(a, blockIdx.x, sh);
+  select_row<NT, KPT>(a, blockIdx.x, sh);
 }
 
-template <int NT, int KPT, bool FLIST = false>
+template <int NT, int KPT>
 static hipError_t launch_kpt(const SelectArgs& a, int rows, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NT, KPT, FLIST>), dim3(rows), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((select_kernel<NT, KPT>), dim3(rows), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---- rows with a scan record: one wave per row ----
+//
+// A filtered candidate list (dense scan) or a gathered row (Refine re-score)
+// whose scan left a record with a boundary bin (or the note that the row
+// holds fewer than topk candidates) is selected in one pass by one wave:
+// every candidate above the boundary bin wins (the record says how many
+// there are), the boundary bin's candidates (at most kFiltBoundaryMax) are
+// collected in LDS and ranked exactly by (score descending, key ascending),
+// the rest of the row is padded with -1.  Excluded entries (-inf, gathered
+// rows only) are in no bin.  Per 64 columns the wave's winners are written
+// to consecutive slots (ballot and mbcnt), so the stores are coalesced, and
+// the next batch of the row is loaded while the current one is classified.
+// No barrier is involved, so many rows are in flight per CU.  Returns false
+// (nothing written) for a row without a usable record.
+__device__ __forceinline__ bool onepass_row_wave(const SelectArgs& a, long long blk, uint32_t* lkey,
+                                                 int* lidx) {
+  const int l = lane_id();
+  const int* fi = a.finfo + kFiltInfoStride * blk;
+  const int bstar = fi[kFiltInfoBoundary];
+  if (bstar == -1) return false;
+  const long long frow = a.row0 + blk;
+  const int b = (int)(frow / a.n_rows), r = (int)(frow % a.n_rows);
+  const float* row = a.scores + blk * a.ld;
+  int* out = a.out + frow * (long long)a.topk;
+  const int* crow;
+  if (a.mode == kModeGather) {
+    const int n_g = (a.n_q + a.group - 1) / a.group;
+    crow = a.cand + ((long long)b * n_g + r / a.group) * a.n_cols;
+  } else {
+    crow = a.lidx + blk * a.ld;
+  }
+  const int n = min(fi[kFiltInfoCount], a.n_cols), base = fi[kFiltInfoBase];
+  const bool all = bstar == -2;  // fewer than topk candidates: all of them
+  const int above = all ? n : fi[kFiltInfoAbove];
+  constexpr int E = 16;  // columns per lane per batch
+  auto load = [&](int c0, uint32_t* kk, int* xx) {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int c = max(min(c0 + j * kWave + l, n - 1), 0);
+      kk[j] = load_key(row, c);
+      xx[j] = crow[c];
+    }
+  };
+  uint32_t k[E];
+  int x[E];
+  int wpos = 0, lpos = 0;
+  if (n > 0) load(0, k, x);
+  for (int c0 = 0; c0 < n; c0 += E * kWave) {
+    uint32_t kn[E];
+    int xn[E];
+    const bool more = c0 + E * kWave < n;
+    if (more) load(c0 + E * kWave, kn, xn);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool in = c0 + j * kWave + l < n && k[j] != kKeyExcluded;
+      const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
+      const bool wn = in && (all || bin > bstar);
+      const bool bd = in && !all && bin == bstar;
+      const unsigned long long mw = __ballot(wn), mb = __ballot(bd);
+      const int ow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mw >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mw, 0));
+      const int ob = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
+      if (wn && wpos + ow < a.topk) out[wpos + ow] = x[j];
+      if (bd && lpos + ob < kFiltBoundaryMax) {
+        lkey[lpos + ob] = k[j];
+        lidx[lpos + ob] = x[j];
+      }
+      wpos += __popcll(mw);
+      lpos += __popcll(mb);
+    }
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        k[j] = kn[j];
+        x[j] = xn[j];
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int m = min(lpos, kFiltBoundaryMax), need = all ? 0 : a.topk - above;
+  if (need > 0) {
+    for (int e = l; e < m; e += kWave) {
+      const uint32_t ke = lkey[e];
+      const int ie = lidx[e];
+      int rank = 0;
+      for (int f = 0; f < m; ++f) {
+        const uint32_t kf = lkey[f];
+        rank += (kf > ke || (kf == ke && lidx[f] < ie)) ? 1 : 0;
+      }
+      if (rank < need) out[above + rank] = ie;
+    }
+  }
+  const int filled = min(a.topk, all ? n : above + min(need, m));
+  for (int i = filled + l; i < a.topk; i += kWave) out[i] = -1;
+  return true;
+}
+
+// Four rows per 256-thread workgroup, one per wave; rows without a usable
+// record then run the general select (rows streamed from global memory),
+// one after another with the whole workgroup.
+__global__ __launch_bounds__(256, 5) void onepass_select_kernel(SelectArgs a, long long n_launch_rows) {
+  __shared__ SelectShared sh;
+  static_assert(4 * kFiltBoundaryMax <= kListCap, "per-wave boundary lists in the shared list");
+  const int wave = threadIdx.x / kWave;
+  const long long blk = (long long)blockIdx.x * 4 + wave;
+  const bool done = blk >= n_launch_rows ||
+                    onepass_row_wave(a, blk, sh.lkey + wave * kFiltBoundaryMax, sh.lidx + wave * kFiltBoundaryMax);
+  if (lane_id() == 0) sh.wscan[wave] = done ? 0 : 1;
+  __syncthreads();
+  int pending = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) pending |= sh.wscan[w] << w;
+  __syncthreads();
+  for (int w = 0; w < 4; ++w) {
+    if ((pending >> w) & 1) {
+      select_row<256, 0>(a, (unsigned)(blockIdx.x * 4 + w), sh);
+      __syncthreads();
+    }
+  }
+}
+
+static hipError_t launch_onepass(const SelectArgs& a, int rows, hipStream_t st) {
+  hipLaunchKernelGGL(onepass_select_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, a, (long long)rows);
   return hipGetLastError();
 }
 
@@ -34,13 +159,10 @@ hipError_t launch_select(const SelectArgs& a, int n_launch_rows, hipStream_t st)
   // candidate lists (up to a few k (1 + ln(n / k)) entries) are held 32 keys
   // per thread by 256-thread workgroups, more rows in flight per CU than
   // with 512 threads; a longer list streams inside the kernel
-  if (a.mode == kModeList) return a.finfo ? launch_kpt<256, 32, true>(a, n_launch_rows, st)
-                                          : launch_kpt<256, 32>(a, n_launch_rows, st);
-  // gathered rows with their scan's records: the one-pass variant (its
-  // general path keeps 8192 keys in registers; 16384 for longer rows)
-  if (a.mode == kModeGather && a.finfo)
-    return a.n_cols <= 256 * 32 ? launch_kpt<256, 32, true>(a, n_launch_rows, st)
-                                : launch_kpt<1024, 16, true>(a, n_launch_rows, st);
+  if (n_launch_rows <= 0) return hipSuccess;
+  // rows with their scan's records (filtered lists, gathered rows): one wave per row
+  if ((a.mode == kModeList || a.mode == kModeGather) && a.finfo) return launch_onepass(a, n_launch_rows, st);
+  if (a.mode == kModeList) return launch_kpt<256, 32>(a, n_launch_rows, st);
   if (a.mode == kModeGather || n_launch_rows <= 0) return launch_by_length(a, n_launch_rows, a.n_cols, st);
   const int classes[4] = {256 * 8, 256 * 32, 1024 * 16, 1024 * 32};
   long long r = 0;

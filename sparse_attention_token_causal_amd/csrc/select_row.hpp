@@ -102,14 +102,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, SelectShared& 
 // NT threads per row; blk is the row within the launch.  KPT > 0: each
 // thread keeps the keys of columns tid + i*NT (i < KPT) in registers.
 // KPT == 0: rows of any length, re-read from global memory in batches of 8
-// loads per thread.  FLIST: the variant for filtered candidate lists with
-// their scan records (the one-pass path, reading 16 entries per thread per
-// batch); the other variants do not contain that path.
+// loads per thread.  (Rows whose scan left a record take the one-pass
+// select of select.hip first; this is their general path.)
 // A row's select is a chain of short dependent phases (loads, reductions,
 // histogram, scans), so rows in flight per CU decide its speed: 256-thread
 // workgroups are held to at least four waves per SIMD (at most 128 VGPRs,
 // four rows per CU; the LDS would allow five).
-template <int NT, int KPT, bool FLIST = false>
+template <int NT, int KPT>
 __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned blk, SelectShared& sh) {
   constexpr int kSelectThreads = NT;
   constexpr int kNW = NT / kWave;
@@ -124,75 +123,6 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
   }
   if (a.mode == kModeList) crow = a.lidx + (long long)blk * a.ld;
   const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-  if (FLIST && (a.mode == kModeList || a.mode == kModeGather) && a.finfo) {
-    // A filtered list (or a gathered row) with its scan's record: one pass
-    // writes every candidate above the boundary bin (there are exactly
-    // `above` of them), collects the boundary bin's candidates (at most
-    // kFiltBoundaryMax), and those are ranked exactly by (score descending,
-    // key ascending).  Excluded entries (-inf, gathered rows only) are in
-    // no bin.
-    const int* fi = a.finfo + kFiltInfoStride * (long long)blk;
-    const int bstar = fi[kFiltInfoBoundary];
-    if (bstar != -1) {
-      const int n = min(fi[kFiltInfoCount], a.n_cols), base = fi[kFiltInfoBase];
-      const bool all = bstar == -2;  // fewer than topk candidates: all of them
-      const int above = all ? n : fi[kFiltInfoAbove];
-      if (tid == 0) sh.list_n = 0;
-      __syncthreads();
-      int wbase = 0;
-      for (int c0 = 0; c0 < n; c0 += 16 * NT) {
-        uint32_t k[16];
-        int x[16], win = 0;
-        bool bnd[16], wn[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int c = min(c0 + j * NT + tid, n - 1);
-          k[j] = load_key(row, c);
-          x[j] = crow[c];
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const bool in = c0 + j * NT + tid < n && k[j] != kKeyExcluded;
-          const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
-          wn[j] = in && (all || bin > bstar);
-          bnd[j] = in && !all && bin == bstar;
-          win += wn[j] ? 1 : 0;
-        }
-        int tot;
-        int pos = wbase + block_excl_scan<NT>(win, &tot, sh);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (wn[j]) {
-            if (pos < a.topk) out[pos] = x[j];
-            ++pos;
-          }
-          if (bnd[j]) {
-            const int p = atomicAdd(&sh.list_n, 1);
-            if (p < kListCap) {
-              sh.lkey[p] = k[j];
-              sh.lidx[p] = x[j];
-            }
-          }
-        }
-        wbase += tot;
-      }
-      __syncthreads();
-      const int m = min(sh.list_n, kListCap), need = all ? 0 : a.topk - above;
-      for (int e = tid; e < m; e += NT) {
-        const uint32_t ke = sh.lkey[e];
-        const int ie = sh.lidx[e];
-        int rank = 0;
-        for (int f = 0; f < m; ++f) {
-          const uint32_t kf = sh.lkey[f];
-          rank += (kf > ke || (kf == ke && sh.lidx[f] < ie)) ? 1 : 0;
-        }
-        if (rank < need) out[above + rank] = ie;
-      }
-      const int filled = min(a.topk, all ? n : above + min(need, m));
-      for (int i = filled + tid; i < a.topk; i += NT) out[i] = -1;
-      return;
-    }
-  }
   int len;
   if (a.mode == kModeList && a.seg_counts) {
     // Segmented list: segment s of the row holds seg_counts[s] entries from

@@ -33,7 +33,7 @@ CASES = [
     # scores that rise with the key position
     Workload("rec_ramp_fp8_L800_G32_C400_k64", 1, 800, 800, 64, 128, "fp8", "fp8", "ar1", "ramp", rho=0.99,
              topk=64, group=32, n_cand=400, seed=44),
-    # candidate rows longer than 8192 columns (the select's wider variant)
+    # candidate rows longer than 8192 columns
     Workload("rec_bf16_L64_n12000_G64_C10000_k300", 1, 64, 12000, 64, 128, "bf16", "bf16", "ar1", "heavy",
              rho=0.98, topk=300, group=64, n_cand=10000, seed=45),
 ]
