@@ -247,14 +247,22 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
   // them; the rescan counts the interval's keys in `hist` (bins of
   // 2^r_shift above r_lo) and, on a tied interval, c_cnt of its keys so far.
   // (after the candidate indices when the columns are gathered)
-  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES + (GATHER ? (a.kc * 4 + 15) / 16 * 16 : 0)) + wave * kFiltBins;
+  // The records of gathered rows count at most kCandLdsMax columns per row,
+  // so their bins are 16-bit counters, two per word (the filtering scan and
+  // the rescan count up to a whole prefix: one word per bin).
+  constexpr int HW = FILTER == 3 ? kFiltBins / 2 : kFiltBins;  // histogram words per wave
+  static_assert(kCandLdsMax < 65536, "a record's bin counts fit 16 bits");
+  uint32_t* hist = (uint32_t*)(smem + 2 * TILE_BYTES + (GATHER ? (a.kc * 4 + 15) / 16 * 16 : 0)) + wave * HW;
+  auto hist_count = [&](int bin) -> int {
+    return FILTER == 3 ? (int)((hist[bin >> 1] >> (16 * (bin & 1))) & 0xFFFFu) : (int)hist[bin];
+  };
   int f_base = 0, f_theta = 0, f_above = 0, f_cnt = 0, c_cnt = 0;
   float f_lo = neg_inf();  // lower edge of bin f_theta (-inf while f_theta == 0)
   bool f_based = false;
   float* f_val = nullptr;
   int* f_idx = nullptr;
   if constexpr (FILTER != 0) {
-    for (int i = l; i < kFiltBins; i += kWave) hist[i] = 0;
+    for (int i = l; i < HW; i += kWave) hist[i] = 0;
     if constexpr (FILTER != 3) {
       f_val = a.cval + crow * a.cld;
       f_idx = a.cidx + crow * a.cld;
@@ -456,7 +464,10 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
               f_based = true;
             }
           }
-          if (ok) atomicAdd(&hist[min(max((int)(order_key(val) >> 15) - f_base, 0), kFiltBins - 1)], 1u);
+          if (ok) {
+            const int bin = min(max((int)(order_key(val) >> 15) - f_base, 0), kFiltBins - 1);
+            atomicAdd(&hist[bin >> 1], 1u << (16 * (bin & 1)));
+          }
         }
       } else if constexpr (FILTER == 2) {
         // Rescan: keys above the interval are always stored; the interval's
@@ -633,7 +644,7 @@ __global__ __launch_bounds__(NWV * 64) void score_kernel(ScoreArgs a) {
     above = 0;
     cnt_b = 0;
     for (int hi = kFiltBins; hi > 0; hi -= kWave) {
-      const int h = (int)hist[hi - 1 - l];  // lane j: bin hi - 1 - j (from the top)
+      const int h = hist_count(hi - 1 - l);  // lane j: bin hi - 1 - j (from the top)
       const int incl = wave_incl_scan(h);
       const unsigned long long m = __ballot(above + incl >= need);
       if (m) {
@@ -793,8 +804,9 @@ size_t score_lds_bytes(int qf, int kf, int D, int rw, int nw, int filter, int ga
   (void)kf;
   // double-buffered tiles, the workgroup's candidate key indices (gather),
   // then one filtering histogram and one flag per wave
+  // (16-bit bins for the records of gathered rows)
   return 2 * ((size_t)tw * (D * ke + 16) + (size_t)tw * 8) + ((size_t)gather_cols * 4 + 15) / 16 * 16 +
-         (filter ? (size_t)nw * (kFiltBins * 4 + 4) : 0);
+         (filter ? (size_t)nw * ((filter == 3 ? kFiltBins * 2 : kFiltBins * 4) + 4) : 0);
 }
 
 hipError_t launch_score(const ScoreArgs& a, int qf, int kf, int H, int D, int n_col_chunks,

@@ -36,6 +36,12 @@ CASES = [
     # candidate rows longer than 8192 columns
     Workload("rec_bf16_L64_n12000_G64_C10000_k300", 1, 64, 12000, 64, 128, "bf16", "bf16", "ar1", "heavy",
              rho=0.98, topk=300, group=64, n_cand=10000, seed=45),
+    # the longest candidate rows one workgroup holds (16384 columns): the
+    # records' histograms are 16-bit counters
+    Workload("rec_bf16_L64_n20000_G64_C16384_k700", 1, 64, 20000, 64, 128, "bf16", "bf16", "ar1", "heavy",
+             rho=0.98, topk=700, group=64, n_cand=16384, seed=46),
+    Workload("rec_fp8_L32_n18000_G32_C16384_k2048", 1, 32, 18000, 64, 128, "fp8", "fp8", "ar1", "heavy",
+             rho=0.99, topk=2048, group=32, n_cand=16384, seed=47),
 ]
 
 
