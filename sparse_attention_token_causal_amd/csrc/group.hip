@@ -9,14 +9,19 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace idx {
 
-// One workgroup per (group, sequence).  Sums run over the members in token
-// order in float32, then divide by the member count; the proxy q is stored
-// as bfloat16 (nearest, ties to even) for BF16/FP8 inputs and as float32 for
-// F32 inputs, the proxy w as float32.  HBM-bound: every q element is read
-// once; each thread owns 16-byte chunks of the (head, dim) row (coalesced
-// across the workgroup) and keeps four members' loads in flight.
+// One workgroup per (group, sequence, part of the (head, dim) row): the row
+// is split over gridDim.z workgroups when there are too few groups to fill
+// the chip (decode: one group per sequence).  Sums run over the members in
+// token order in float32, then divide by the member count; the proxy q is
+// stored as bfloat16 (nearest, ties to even) for BF16/FP8 inputs and as
+// float32 for F32 inputs, the proxy w as float32.  HBM-bound: every q
+// element is read once; each thread owns 16-byte chunks of the row
+// (coalesced across the workgroup) and loads four members at a time (a
+// group of fewer members issues all its loads at once).
 template <int QF>
 __global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const float* q_scale,
                                                           const float* w, int n_q, int H, int D,
@@ -46,28 +51,27 @@ __global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const f
       for (int i = 0; i < 16; ++i) v[i] = fp8_to_f32(((uint32_t)raw[i / 4] >> (8 * (i % 4))) & 0xFFu) * sc;
     }
   };
-  for (size_t ch = threadIdx.x; ch * VEC < HD; ch += blockDim.x) {
+  for (size_t ch = (size_t)blockIdx.z * blockDim.x + threadIdx.x; ch * VEC < HD;
+       ch += (size_t)gridDim.z * blockDim.x) {
     float s[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) s[i] = 0.f;
-    int t = t0;
-    for (; t + 4 <= t1; t += 4) {
+    for (int t = t0; t < t1; t += 4) {
+      // four members' loads in flight (past the group's end: its last member
+      // again, not added)
       i32x4 raw[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) raw[u] = *(const i32x4*)(qb + ((size_t)(t + u) * HD + ch * VEC) * EB);
+      for (int u = 0; u < 4; ++u)
+        raw[u] = *(const i32x4*)(qb + ((size_t)min(t + u, t1 - 1) * HD + ch * VEC) * EB);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        float v[VEC];
-        decode(raw[u], t + u, v);
+        if (t + u < t1) {
+          float v[VEC];
+          decode(raw[u], t + u, v);
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) s[i] += v[i];
+          for (int i = 0; i < VEC; ++i) s[i] += v[i];
+        }
       }
-    }
-    for (; t < t1; ++t) {
-      float v[VEC];
-      decode(*(const i32x4*)(qb + ((size_t)t * HD + ch * VEC) * EB), t, v);
-#pragma unroll
-      for (int i = 0; i < VEC; ++i) s[i] += v[i];
     }
     const size_t o = prow * HD + ch * VEC;
     if constexpr (QF == F32) {
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(256) void proxy_build_kernel(const void* q, const f
             i32x4{(int)packed[4 * i], (int)packed[4 * i + 1], (int)packed[4 * i + 2], (int)packed[4 * i + 3]};
     }
   }
-  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+  for (int h = threadIdx.x; h < (blockIdx.z == 0 ? H : 0); h += blockDim.x) {
     float s = 0.f;  // member order, eight loads in flight
     int t = t0;
     for (; t + 8 <= t1; t += 8) {
@@ -102,7 +106,12 @@ hipError_t launch_proxy_build(const void* q, const float* q_scale, const float* 
                               int H, int D, int qf, int group, void* pq, float* pw,
                               hipStream_t st) {
   const int n_g = (n_q + group - 1) / group;
-  dim3 grid(n_g, B);
+  // parts of the (head, dim) row: about 256 workgroups in all, each thread at
+  // least one 16-byte chunk
+  const long long chunks = (long long)H * D * (qf == F32 ? 4 : (qf == BF16 ? 2 : 1)) / 16;
+  long long parts = std::max(1LL, 256LL / ((long long)n_g * B));
+  parts = std::min(parts, std::max(1LL, chunks / 256));
+  dim3 grid(n_g, B, (unsigned)parts);
   if (qf == F32)
     hipLaunchKernelGGL(proxy_build_kernel<F32>, grid, dim3(256), 0, st, q, q_scale, w, n_q, H, D, group, pq, pw);
   else if (qf == BF16)
