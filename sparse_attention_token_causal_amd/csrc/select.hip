@@ -52,12 +52,18 @@ __device__ __forceinline__ bool onepass_row_wave(const SelectArgs& a, long long 
   const bool all = bstar == -2;  // fewer than topk candidates: all of them
   const int above = all ? n : fi[kFiltInfoAbove];
   constexpr int E = 16;  // columns per lane per batch
+  // (32-bit byte offsets from the wave's row bases; the columns of a batch
+  // past the row's end are clamped to its last column, only in the last batch)
   auto load = [&](int c0, uint32_t* kk, int* xx) {
+    const bool whole = c0 + E * kWave <= n;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const int c = max(min(c0 + j * kWave + l, n - 1), 0);
-      kk[j] = load_key(row, c);
-      xx[j] = crow[c];
+      int c = c0 + j * kWave + l;
+      if (!whole) c = max(min(c, n - 1), 0);
+      const uint32_t off = (uint32_t)c * 4u;
+      const float v = *(const float*)((const char*)row + off);
+      kk[j] = v == neg_inf() ? kKeyExcluded : order_key(v);
+      xx[j] = *(const int*)((const char*)crow + off);
     }
   };
   uint32_t k[E];
@@ -72,13 +78,14 @@ __device__ __forceinline__ bool onepass_row_wave(const SelectArgs& a, long long 
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       const bool in = c0 + j * kWave + l < n && k[j] != kKeyExcluded;
-      const int bin = min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1);
-      const bool wn = in && (all || bin > bstar);
-      const bool bd = in && !all && bin == bstar;
-      const unsigned long long mw = __ballot(wn), mb = __ballot(bd);
+      // an entry outside the row or excluded is in bin -1; with fewer than
+      // topk candidates (bstar == -2) every other entry lies above bstar
+      const int bin = in ? min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1) : -1;
+      const bool wn = bin > bstar, bd = bin == bstar;
+      const unsigned long long mw = __ballot(bin > bstar), mb = __ballot(bin == bstar);
       const int ow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mw >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mw, 0));
       const int ob = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
-      if (wn && wpos + ow < a.topk) out[wpos + ow] = x[j];
+      if (wn && wpos + ow < a.topk) *(int*)((char*)out + (uint32_t)(wpos + ow) * 4u) = x[j];
       if (bd && lpos + ob < kFiltBoundaryMax) {
         lkey[lpos + ob] = k[j];
         lidx[lpos + ob] = x[j];
@@ -119,7 +126,7 @@ __device__ __forceinline__ bool onepass_row_wave(const SelectArgs& a, long long 
 __global__ __launch_bounds__(256, 5) void onepass_select_kernel(SelectArgs a, long long n_launch_rows) {
   __shared__ SelectShared sh;
   static_assert(4 * kFiltBoundaryMax <= kListCap, "per-wave boundary lists in the shared list");
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const long long blk = (long long)blockIdx.x * 4 + wave;
   const bool done = blk >= n_launch_rows ||
                     onepass_row_wave(a, blk, sh.lkey + wave * kFiltBoundaryMax, sh.lidx + wave * kFiltBoundaryMax);
