@@ -52,52 +52,82 @@ __device__ __forceinline__ bool onepass_row_wave(const SelectArgs& a, long long 
   const bool all = bstar == -2;  // fewer than topk candidates: all of them
   const int above = all ? n : fi[kFiltInfoAbove];
   constexpr int E = 16;  // columns per lane per batch
-  // (32-bit byte offsets from the wave's row bases; the columns of a batch
-  // past the row's end are clamped to its last column, only in the last batch)
-  auto load = [&](int c0, uint32_t* kk, int* xx) {
+  // The boundary bin as a float interval [f_lo, f_hi): a key lies above the
+  // bin exactly when its value is >= f_hi, in it when it is >= f_lo and
+  // below f_hi (order keys are monotone in the value and map -0 to +0, and
+  // the bin edges, multiples of 2^15, clamped to the keys of -FLT_MAX and
+  // +inf, are keys of floats).  The edge bins also hold the keys clamped
+  // into them: below the window for bin 0 (f_lo = -FLT_MAX), above it for
+  // the last bin (f_hi NaN: no value compares >= it).  Excluded (-inf)
+  // entries lie below both.  With fewer than topk candidates every other
+  // entry lies above f_hi.
+  float f_lo, f_hi;
+  if (all) {
+    f_hi = -__FLT_MAX__;
+    f_lo = __builtin_huge_valf();
+  } else {
+    auto edge = [](long long kb) -> float {
+      return key_to_float((uint32_t)min(max(kb, 0x00800000LL), 0xFF800000LL));
+    };
+    const long long kb = (long long)(bstar + base) * 32768LL;
+    f_lo = bstar == 0 ? -__FLT_MAX__ : edge(kb);
+    f_hi = bstar == kFiltBins - 1 ? __builtin_nanf("") : edge(kb + 32768LL);
+  }
+  // (32-bit byte offsets from the wave's row bases; in a row's last batch
+  // the columns past its end read its last column and count as excluded)
+  auto load = [&](int c0, float* vv, int* xx) {
     const bool whole = c0 + E * kWave <= n;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
       int c = c0 + j * kWave + l;
       if (!whole) c = max(min(c, n - 1), 0);
       const uint32_t off = (uint32_t)c * 4u;
-      const float v = *(const float*)((const char*)row + off);
-      kk[j] = v == neg_inf() ? kKeyExcluded : order_key(v);
+      vv[j] = *(const float*)((const char*)row + off);
       xx[j] = *(const int*)((const char*)crow + off);
     }
   };
-  uint32_t k[E];
-  int x[E];
   int wpos = 0, lpos = 0;
-  if (n > 0) load(0, k, x);
-  for (int c0 = 0; c0 < n; c0 += E * kWave) {
-    uint32_t kn[E];
-    int xn[E];
-    const bool more = c0 + E * kWave < n;
-    if (more) load(c0 + E * kWave, kn, xn);
+  auto classify = [&](int c0, float* v, const int* x) {
+    if (c0 + E * kWave > n) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (c0 + j * kWave + l >= n) v[j] = neg_inf();
+    }
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const bool in = c0 + j * kWave + l < n && k[j] != kKeyExcluded;
-      // an entry outside the row or excluded is in bin -1; with fewer than
-      // topk candidates (bstar == -2) every other entry lies above bstar
-      const int bin = in ? min(max((int)(k[j] >> 15) - base, 0), kFiltBins - 1) : -1;
-      const bool wn = bin > bstar, bd = bin == bstar;
-      const unsigned long long mw = __ballot(bin > bstar), mb = __ballot(bin == bstar);
+      // (each ballot is of one compare)
+      const bool wn = v[j] >= f_hi;
+      const unsigned long long mw = __ballot(v[j] >= f_hi), mb = __ballot(v[j] >= f_lo) & ~mw;
       const int ow = __builtin_amdgcn_mbcnt_hi((uint32_t)(mw >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mw, 0));
-      const int ob = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
       if (wn && wpos + ow < a.topk) *(int*)((char*)out + (uint32_t)(wpos + ow) * 4u) = x[j];
-      if (bd && lpos + ob < kFiltBoundaryMax) {
-        lkey[lpos + ob] = k[j];
-        lidx[lpos + ob] = x[j];
+      if (mb) {
+        const int ob = __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0));
+        if (((mb >> l) & 1ull) && lpos + ob < kFiltBoundaryMax) {
+          lkey[lpos + ob] = order_key(v[j]);
+          lidx[lpos + ob] = x[j];
+        }
+        lpos += __popcll(mb);
       }
       wpos += __popcll(mw);
-      lpos += __popcll(mb);
     }
-    if (more) {
+  };
+  // the next batch's loads are issued before this batch is classified
+  if (n > 0) {
+    float v[E];
+    int x[E];
+    load(0, v, x);
+    for (int c0 = 0; c0 < n; c0 += E * kWave) {
+      float vn[E];
+      int xn[E];
+      const bool more = c0 + E * kWave < n;
+      if (more) load(c0 + E * kWave, vn, xn);
+      classify(c0, v, x);
+      if (more) {
 #pragma unroll
-      for (int j = 0; j < E; ++j) {
-        k[j] = kn[j];
-        x[j] = xn[j];
+        for (int j = 0; j < E; ++j) {
+          v[j] = vn[j];
+          x[j] = xn[j];
+        }
       }
     }
   }
