@@ -169,10 +169,6 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
     len = row_length(a, r, blk);
   }
   constexpr int REG = KPT > 0 ? KPT : 1;
-  // loads per thread in flight per batch of a streamed row (the 1024-thread
-  // streaming variant, one row per CU, is bound by the bytes in flight; the
-  // 256-thread one inside the one-wave select's kernel keeps its registers)
-  constexpr int SB = (KPT == 0 && NT == 1024) ? 16 : 8;
   uint32_t keys[REG];
   // rows longer than the register tile (possible for candidate lists) stream
   const bool regs = KPT > 0 && len <= REG * kSelectThreads;
@@ -192,17 +188,17 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         f(c, keys[i], indexed ? idxs[i] : c);
       }
     } else {
-      for (int c0 = 0; c0 < len; c0 += SB * kSelectThreads) {
-        float v[SB];
-        int x[SB];
+      for (int c0 = 0; c0 < len; c0 += 8 * kSelectThreads) {
+        float v[8];
+        int x[8];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const int cc = min(c0 + j * kSelectThreads + tid, max(len - 1, 0));
           v[j] = row[cc];
           x[j] = indexed ? crow[cc] : cc;
         }
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const int c = c0 + j * kSelectThreads + tid;
           f(c, (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded, x[j]);
         }
@@ -475,18 +471,18 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         sh.out_n = 0;
       }
       __syncthreads();
-      for (int c0 = 0; c0 < len; c0 += SB * kSelectThreads) {
-        float v[SB];
-        int x[SB];
+      for (int c0 = 0; c0 < len; c0 += 8 * kSelectThreads) {
+        float v[8];
+        int x[8];
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const int cc = min(c0 + j * kSelectThreads + tid, max(len - 1, 0));
           v[j] = row[cc];
           x[j] = indexed ? crow[cc] : cc;
         }
         uint32_t cm = 0;
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
+        for (int j = 0; j < 8; ++j) {
           const int c = c0 + j * kSelectThreads + tid;
           const uint32_t k = (c < len && v[j] != neg_inf()) ? order_key(v[j]) : kKeyExcluded;
           cm |= (uint32_t)certain(k) << j;
@@ -503,7 +499,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         if (lane == kWave - 1 && wt) base = atomicAdd(&sh.out_n, wt);
         int pos = __builtin_amdgcn_readlane(base, kWave - 1) + incl - n;
 #pragma unroll
-        for (int j = 0; j < SB; ++j)
+        for (int j = 0; j < 8; ++j)
           if ((cm >> j) & 1u) out[pos++] = x[j];
       }
       if (gather_late) {
