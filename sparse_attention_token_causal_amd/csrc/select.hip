@@ -5,8 +5,11 @@
 
 namespace idx {
 
+// The 1024-thread streaming variant (rows longer than any register tile)
+// is held to 64 VGPRs so that two rows run per CU: one row's loads in
+// flight do not cover the memory latency by themselves.
 template <int NT, int KPT>
-__global__ __launch_bounds__(NT, NT == 256 ? 4 : 1) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(NT, NT == 256 ? 4 : (KPT == 0 ? 8 : 1)) void select_kernel(SelectArgs a) {
   __shared__ SelectShared sh;
   select_row<NT, KPT>(a, blockIdx.x, sh);
 }
