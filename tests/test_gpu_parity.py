@@ -57,6 +57,13 @@ DENSE = [
              topk=300, seed=23),
     Workload("filter_overflow_int_H64_L4500_k40", 1, 4500, 4500, 64, 64, "bf16", "bf16", "int", "int",
              topk=40, seed=24, w_dist="int"),
+    # every 16th key 2^20 times larger: the first tile's spikes place the
+    # histogram window far above the other keys, which are all clamped into
+    # its lowest bin; rows of up to about 270 keys record that edge bin as
+    # their boundary (the one-wave select's open-ended lower bin), longer
+    # rows take the general select
+    Workload("filter_spikes_H64_L600_k50", 1, 600, 600, 64, 128, "bf16", "bf16", "normal8", "spikes",
+             topk=50, seed=27),
     # at most 4 rows per sequence take the split-key scan + histogram compaction:
     # fp8 x fp8 with a partly empty row-wave, d = 64, ties, k near the prefix
     Workload("split_fp8_B2_nq3_H32_d128", 2, 3, 4099, 32, 128, "fp8", "fp8", "ar1", "heavy", rho=0.99,
