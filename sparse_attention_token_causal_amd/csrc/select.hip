@@ -186,8 +186,10 @@ static hipError_t launch_onepass(const SelectArgs& a, int rows, hipStream_t st) 
 // 256-thread workgroups (more rows in flight per CU than wider ones), unless
 // the launch has too few rows to occupy the chip (fewer than two per CU:
 // decode-sized problems), where a row's chain of phases is the whole time
-// and 1024 threads per row shorten it.
+// and 1024 threads per row shorten it (with no more keys per thread than the
+// row needs: each phase walks every register slot).
 static hipError_t launch_by_length(const SelectArgs& a, int rows, int n, hipStream_t st) {
+  if (rows < 512 && n > 256 * 8 && n <= 1024 * 8) return launch_kpt<1024, 8>(a, rows, st);
   if (rows < 512 && n > 256 * 8 && n <= 1024 * 16) return launch_kpt<1024, 16>(a, rows, st);
   if (n <= 256 * 8) return launch_kpt<256, 8>(a, rows, st);
   if (n <= 256 * 32) return launch_kpt<256, 32>(a, rows, st);
