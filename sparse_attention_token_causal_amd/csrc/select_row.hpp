@@ -224,37 +224,75 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
       keys[i] = (c < len && v[i] != neg_inf()) ? order_key(v[i]) : kKeyExcluded;
     }
   }
-  for_keys([&](int, uint32_t k, int) {
-    if (k != kKeyExcluded) {
-      ++nv;
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
-    }
-  });
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) nv += __shfl_xor(nv, off, kWave);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
-  }
-  if (lane == 0) {
-    sh.wred[0][wave] = nv;
-    sh.wred[1][wave] = (int)kmin;
-    sh.wred[2][wave] = (int)kmax;
-  }
-  __syncthreads();
+  // count, minimum and maximum of the eligible keys that `visit` passes to
+  // its callback, reduced over the workgroup
   int n_valid = 0;
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
+  auto key_stats = [&](auto&& visit) {
+    nv = 0;
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+    visit([&](uint32_t k) {
+      if (k != kKeyExcluded) {
+        ++nv;
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+      }
+    });
 #pragma unroll
-  for (int i = 0; i < kNW; ++i) {
-    n_valid += sh.wred[0][i];
-    kmin = min(kmin, (uint32_t)sh.wred[1][i]);
-    kmax = max(kmax, (uint32_t)sh.wred[2][i]);
+    for (int off = 32; off > 0; off >>= 1) nv += __shfl_xor(nv, off, kWave);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, kWave));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, kWave));
+    }
+    if (lane == 0) {
+      sh.wred[0][wave] = nv;
+      sh.wred[1][wave] = (int)kmin;
+      sh.wred[2][wave] = (int)kmax;
+    }
+    __syncthreads();
+    n_valid = 0;
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < kNW; ++i) {
+      n_valid += sh.wred[0][i];
+      kmin = min(kmin, (uint32_t)sh.wred[1][i]);
+      kmax = max(kmax, (uint32_t)sh.wred[2][i]);
+    }
+    __syncthreads();
+  };
+  // Linear bins over [kmin, kmax] (section 2a) spread the row's values when
+  // this holds.
+  auto spreads = [&](uint32_t lo, uint32_t hi) {
+    const float vlo = key_to_float(lo), vhi = key_to_float(hi);
+    const float scale = (float)(kBins - 1) / (vhi - vlo);
+    return vhi > vlo && scale > 0.f && scale < __builtin_huge_valf();
+  };
+  // A streamed row takes the range of its linear bins from a sample (16
+  // evenly spaced runs of 256 columns) instead of a pass over the row: keys
+  // outside the sample's range fall in the edge bins (the map stays
+  // monotone), each bin's exact key range is still recorded, and the bins'
+  // total is the row's count of eligible keys.  A sample without spread
+  // falls back to the pass.
+  bool sampled = false;
+  if constexpr (KPT == 0) {
+    constexpr int kRun = 256, kRuns = 16;
+    if (len >= 2 * kRun * kRuns) {
+      key_stats([&](auto&& f) {
+        for (int i = tid; i < kRun * kRuns; i += kSelectThreads) {
+          const int c = (int)((long long)(i / kRun) * len / kRuns) + i % kRun;
+          const float v = row[c];
+          f(v != neg_inf() ? order_key(v) : kKeyExcluded);
+        }
+      });
+      // (workgroup-wide values only: the branch below holds barriers)
+      sampled = n_valid > 0 && spreads(kmin, kmax);
+    }
   }
+  if (!sampled) key_stats([&](auto&& f) { for_keys([&](int, uint32_t k, int) { f(k); }); });
   const int topk = a.topk;
-  const int kk = min(topk, n_valid);
+  int kk = min(topk, n_valid);
 
   // ---- 2. narrow the boundary interval [blo, bhi] of keys ----
   // `above` eligible keys lie above the interval and `need` of the keys inside
@@ -290,13 +328,13 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
     return sh.sel_bin;
   };
 
-  if (n_valid > topk) {
+  if (sampled || n_valid > topk) {
     // 2a. one pass of 2048 bins linear in the score value between the row's
     // minimum and maximum (a monotone map: a larger score never lands in a
     // lower bin), which spreads the bulk of a row over many bins
     const float vlo = key_to_float(blo), vhi = key_to_float(bhi);
     const float scale = (float)(kBins - 1) / (vhi - vlo);
-    if (vhi > vlo && scale > 0.f && scale < __builtin_huge_valf()) {
+    if (spreads(blo, bhi)) {
       const float off = -vlo * scale;
       auto lbin = [&](uint32_t k) {
         const float x = __builtin_fmaf(key_to_float(k), scale, off);
@@ -324,6 +362,23 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         }
       });
       __syncthreads();
+      if (sampled) {
+        // the row's count of eligible keys; with at most topk of them every
+        // one wins: the whole key range is the (whole) boundary interval
+        constexpr int BPT = kBins / NT;
+        int s_ = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) s_ += (int)sh.hist[BPT * tid + j];
+        block_excl_scan<NT>(s_, &n_valid, sh);
+        kk = min(topk, n_valid);
+        need = kk;
+        in_bin = n_valid;
+        if (n_valid <= topk) {
+          blo = 1u;  // every eligible key (the excluded key is 0)
+          bhi = 0xFFFFFFFFu;
+        }
+      }
+      if (!sampled || n_valid > topk) {
       int before;
       const uint32_t b = pick_desc(&before);
       above += before;
@@ -360,6 +415,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, const unsigned b
         bhi = max(bhi, (uint32_t)sh.wred[2][i]);
       }
       __syncthreads();
+      }
       }
     }
     // 2b. MSB-first radix descent in 11-bit digits inside [blo, bhi]
