@@ -6,8 +6,9 @@ above it and ranks only that bin; asked for the candidate scores, the same
 scan writes no records and the select runs its general path.  Both select
 the exact top-k of the same float32 scores (ties to the lower key index), so
 the two index sets must agree on every row: tie-heavy rows, rows whose keys
-all rise with position, rows with fewer eligible candidates than k, and
-rows longer than one register tile of the select.
+all rise with position, rows with fewer eligible candidates than k (also
+rows of 8192 slots that are mostly empty), and rows longer than one
+register tile of the select.
 
 Source: "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse
 Attention", Abstract (each query keeps the top-k of its re-scored
@@ -42,6 +43,12 @@ CASES = [
              rho=0.98, topk=700, group=64, n_cand=16384, seed=46),
     Workload("rec_fp8_L32_n18000_G32_C16384_k2048", 1, 32, 18000, 64, 128, "fp8", "fp8", "ar1", "heavy",
              rho=0.99, topk=2048, group=32, n_cand=16384, seed=47),
+    # a budget beyond every prefix: rows of 8192 candidate slots, mostly
+    # empty, and in the groups with fewer than k keys no record, so the
+    # one-pass kernel's general path streams them with a sampled bin range
+    # (most waves' samples hold no eligible key)
+    Workload("rec_sparse_bf16_L2500_G64_C8192_k2048", 1, 2500, 2500, 64, 128, "bf16", "bf16", "ar1", "heavy",
+             rho=0.98, topk=2048, group=64, n_cand=8192, seed=48),
 ]
 
 
